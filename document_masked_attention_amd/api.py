@@ -1,0 +1,234 @@
+"""Thin Python binding of libdocmask.so (C ABI in include/docmask.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch supplies device memory and the current HIP stream.  Tensors
+must be on the current GPU; bf16 tensors may be given as torch.bfloat16 or as
+16-bit integer views of the same bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdocmask.so")
+_lib = None
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE_INPUT = 0, -1, -2, -3, -4, -5
+OP_FWD, OP_BWD = 1, 2
+ACCUMULATE_DQ = 1
+MAX_CHUNKS = 256
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+
+class Chunk(ctypes.Structure):
+    _fields_ = [("g_start", ctypes.c_int32), ("len", ctypes.c_int32)]
+
+
+_SIGNATURES = {
+    "docmask_workspace_size": (_sz, [ctypes.c_int, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "docmask_schedule_workspace_size": (_sz, [_vp, _i32, _i32, _i32, _i32, _i32]),
+    "docmask_schedule": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _sz, _vp]),
+    "docmask_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                        _vp, _vp, _vp, _sz, _vp]),
+    "docmask_attn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _f32, _vp, _vp, _vp, ctypes.c_int, _vp, _sz, _vp]),
+    "lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "docmask_check_errors": (ctypes.c_int, [_vp, _vp]),
+    "docmask_f32_to_bf16": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
+    "docmask_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class DocmaskError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m document_masked_attention_amd.build`")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def strerror(status: int) -> str:
+    return lib().docmask_strerror(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise DocmaskError(status, what)
+
+
+def _chunks(chunks):
+    n = len(chunks)
+    arr = (Chunk * max(n, 1))()
+    for i, (g, length) in enumerate(chunks):
+        arr[i].g_start = int(g)
+        arr[i].len = int(length)
+    return arr, n
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected bf16 data, got {t.dtype}")
+
+
+def _dev_i32(x, device) -> torch.Tensor:
+    if isinstance(x, torch.Tensor):
+        if x.dtype != torch.int32 or x.device.type != "cuda":
+            raise TypeError("cu_seqlens must be an int32 tensor on the GPU")
+        return x
+    return torch.as_tensor(x, dtype=torch.int32, device=device)
+
+
+def workspace_size(op: int, n_docs: int, chunks, kv_lo: int, kv_hi: int, hq: int, hkv: int, d: int) -> int:
+    arr, n = _chunks(chunks)
+    return int(lib().docmask_workspace_size(op, n_docs, arr, n, kv_lo, kv_hi, hq, hkv, d))
+
+
+def schedule_workspace_size(chunks, kv_lo: int, kv_hi: int, bq: int, bk: int) -> int:
+    arr, n = _chunks(chunks)
+    return int(lib().docmask_schedule_workspace_size(arr, n, kv_lo, kv_hi, bq, bk))
+
+
+def schedule(cu_seqlens, chunks, kv_lo: int, kv_hi: int, bq: int, bk: int, device="cuda") -> dict:
+    """Run the tile scheduler and return its outputs as device tensors."""
+    cu = _dev_i32(cu_seqlens, device)
+    n_qt = sum((n + bq - 1) // bq for _, n in chunks)
+    n_kt = (kv_hi - kv_lo + bk - 1) // bk
+    out = {
+        "qtile_desc": torch.empty((n_qt, 4), dtype=torch.int32, device=cu.device),
+        "kvtile_desc": torch.empty((n_kt, 4), dtype=torch.int32, device=cu.device),
+        "need": torch.empty((len(chunks), 2), dtype=torch.int32, device=cu.device),
+        "lpt_q": torch.empty(n_qt, dtype=torch.int32, device=cu.device),
+        "lpt_kv": torch.empty(n_kt, dtype=torch.int32, device=cu.device),
+        "counters": torch.empty(4, dtype=torch.int64, device=cu.device),
+    }
+    ws_bytes = schedule_workspace_size(chunks, kv_lo, kv_hi, bq, bk)
+    if ws_bytes == 0:
+        raise DocmaskError(EINVAL, "docmask_schedule_workspace_size")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=cu.device)
+    arr, n = _chunks(chunks)
+    st = lib().docmask_schedule(_ptr(cu), cu.numel() - 1, arr, n, kv_lo, kv_hi, bq, bk,
+                                _ptr(out["qtile_desc"]), _ptr(out["kvtile_desc"]), _ptr(out["need"]),
+                                _ptr(out["lpt_q"]), _ptr(out["lpt_kv"]), _ptr(out["counters"]),
+                                _ptr(ws), ws_bytes, _stream())
+    _check(st, "docmask_schedule")
+    out["workspace"] = ws
+    return out
+
+
+def attn_fwd(q, k, v, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float | None = None,
+             out=None, lse=None, workspace=None):
+    """O [Tq, Hq, D] (bf16) and LSE [Hq, Tq] (float32) of document-masked attention."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    cu = _dev_i32(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    n_docs = cu.numel() - 1
+    ws_bytes = workspace_size(OP_FWD, n_docs, chunks, kv_lo, kv_hi, hq, hkv, d)
+    if ws_bytes == 0:
+        raise DocmaskError(EINVAL, "docmask_workspace_size")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    arr, n = _chunks(chunks)
+    st = lib().docmask_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_docs, arr, n, kv_lo, kv_hi, hq, hkv, d,
+                                float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "docmask_attn_fwd")
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, d_o, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float | None = None,
+             dq=None, dk=None, dv=None, accumulate_dq: bool = False, workspace=None):
+    """float32 dQ [Tq, Hq, D], dK and dV [Tkv, Hkv, D]."""
+    q, k, v, o, d_o = _bits(q), _bits(k), _bits(v), _bits(o), _bits(d_o)
+    tq, hq, d = q.shape
+    tkv, hkv, _ = k.shape
+    cu = _dev_i32(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if dq is None:
+        dq = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((tkv, hkv, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((tkv, hkv, d), dtype=torch.float32, device=q.device)
+    n_docs = cu.numel() - 1
+    ws_bytes = workspace_size(OP_BWD, n_docs, chunks, kv_lo, kv_hi, hq, hkv, d)
+    if ws_bytes == 0:
+        raise DocmaskError(EINVAL, "docmask_workspace_size")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    arr, n = _chunks(chunks)
+    st = lib().docmask_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(cu), n_docs, arr, n,
+                                kv_lo, kv_hi, hq, hkv, d, float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                ACCUMULATE_DQ if accumulate_dq else 0, _ptr(workspace), workspace.numel(),
+                                _stream())
+    _check(st, "docmask_attn_bwd")
+    return dq, dk, dv
+
+
+def lse_merge(o_parts, lse_parts, o_out=None, lse_out=None):
+    """Merge partials o_parts [P, rows, hq, d] (bf16), lse_parts [P, hq, rows]."""
+    o_parts = _bits(o_parts)
+    n_parts, rows, hq, d = o_parts.shape
+    if o_out is None:
+        o_out = torch.empty((rows, hq, d), dtype=torch.bfloat16, device=o_parts.device)
+    if lse_out is None:
+        lse_out = torch.empty((hq, rows), dtype=torch.float32, device=o_parts.device)
+    st = lib().lse_merge(_ptr(o_parts), _ptr(lse_parts), n_parts, rows, hq, d, _ptr(o_out), _ptr(lse_out),
+                         _stream())
+    _check(st, "lse_merge")
+    return o_out, lse_out
+
+
+def check_errors(workspace) -> int:
+    """Synchronise and return the device-side input status of a workspace."""
+    return int(lib().docmask_check_errors(_ptr(workspace), _stream()))
+
+
+def f32_to_bf16(src: torch.Tensor, out=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    st = lib().docmask_f32_to_bf16(_ptr(src), _ptr(out), src.numel(), _stream())
+    _check(st, "docmask_f32_to_bf16")
+    return out

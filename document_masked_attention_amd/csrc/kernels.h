@@ -1,0 +1,80 @@
+// Kernel parameter blocks and launchers (internal to libdocmask).
+#pragma once
+
+#include "common.h"
+
+namespace docmask {
+
+struct SchedParams {
+  ChunkTable ch;
+  int32_t kv_lo, kv_hi, bq, bk, n_qtiles, n_kvtiles;
+  const int32_t* cu;
+  int32_t n_docs;
+  int32_t needed_end;              // largest global position + 1 any call touches
+  int32_t* plan_q;                 // [n_qtiles][QP_WORDS] or null
+  int32_t* qdesc;                  // [n_qtiles][4] or null
+  int32_t* kvdesc;                 // [n_kvtiles][4] or null
+  int32_t* need;                   // [n_chunks][2] or null
+  int32_t* key_q;                  // [n_qtiles] or null
+  int32_t* key_kv;                 // [n_kvtiles] or null
+  unsigned long long* counters;    // [4] or null
+  int32_t* err;                    // workspace error word
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int32_t* cu;
+  const int32_t* plan;   // [n_qtiles][QP_WORDS]
+  const int32_t* lpt;    // [n_qtiles]
+  const int32_t* err;
+  int32_t n_docs, n_qtiles, hq, hkv, group, n_hb, kv_lo, kv_hi, tq, xcd_cluster;
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+struct MergeParams {
+  const uint16_t* o_parts;   // [P][rows][hq][D]
+  const float* lse_parts;    // [P][hq][rows]
+  uint16_t* o_out;           // [rows][hq][D]
+  float* lse_out;            // [hq][rows]
+  int32_t n_parts, rows, hq;
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* d_o;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;          // [hq][tq] workspace
+  const int32_t* cu;
+  const int32_t* plan_q;  // [n_qtiles][QP_WORDS] with bq = kBwdBQ
+  const int32_t* kvdesc;  // [n_kvtiles][4] with bk = kBwdBK
+  const int32_t* lpt_kv;  // [n_kvtiles]
+  const int32_t* err;
+  int32_t n_docs, n_qtiles, n_kvtiles, hq, hkv, group, kv_lo, kv_hi, tq, xcd_cluster;
+  float scale;           // softmax scale
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+constexpr int kFwdBK = 64;
+constexpr int kBwdBQ = 32;
+constexpr int kBwdBK = 128;
+
+hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv, int32_t* hist,
+                           hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream);
+int fwd_rows_per_tile(int group);
+hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
+hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, hipStream_t stream);
+
+}  // namespace docmask

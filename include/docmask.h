@@ -1,0 +1,170 @@
+/*
+ * docmask.h - C ABI of libdocmask.so: document-masked (intra-document causal)
+ * attention over a packed variable-length sequence, as one context-parallel
+ * rank computes it, on AMD Instinct MI355X (gfx950).
+ *
+ * Definitions come from public pages on context parallelism:
+ *  - "FlashCP: Load-Balanced Communication-Efficient Context Parallelism for
+ *    LLM Training", section 2.1 and Figure 1(a): documents are packed into one
+ *    sequence and a query attends only to keys of its own document that are
+ *    not after it (the diagonal is included, as the shard workload
+ *    W = (2p + s + 1) s / 2 of section 3.1 counts it).  Section 2.2: a CP
+ *    worker holds several query chunks (2 x CP chunking) and sees the KV of
+ *    other workers.
+ *  - "LLM Context Parallel in Production": document boundaries travel as
+ *    cumulative-length arrays; results over separate KV blocks are combined
+ *    with the row maximum and exponential sum (online softmax); kernels skip
+ *    blocks with no valid pair and the effective block count is logged.
+ *
+ * Conventions shared by every call
+ *  - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16).
+ *  - Q, O, dO: [Tq][Hq][D] row-major, where the Tq local query rows are the
+ *    chunks concatenated in list order.  K, V: [Tkv][Hkv][D] with
+ *    Tkv = kv_hi - kv_lo; row r holds global position kv_lo + r.
+ *  - LSE: float [Hq][Tq], natural log of the sum of exp(score).
+ *  - cu_seqlens: device int32 [n_docs + 1], cu[0] = 0, non-decreasing; the
+ *    documents cover every global position a call touches.
+ *  - GQA: query head h reads KV head h / (Hq / Hkv).
+ *  - A query row with no allowed key in [kv_lo, kv_hi) gets O = 0 and
+ *    LSE = -inf.
+ *  - Every pointer argument named *_dev or a tensor is device memory owned by
+ *    the caller; chunk arrays are host memory read during the call.  The
+ *    library allocates nothing and keeps no state between calls; it is
+ *    re-entrant.  Calls on one stream run in order; calls that share a
+ *    workspace must not overlap.
+ *  - Work is enqueued on `stream` (0 = the null stream).  The return value
+ *    reports argument validation (checked on the host before anything is
+ *    enqueued) and launch errors; device-side input errors (malformed
+ *    cu_seqlens) are recorded in the workspace and read back with
+ *    docmask_check_errors.
+ *  - Tensor pointers must be 16-byte aligned; D must be 64 or 128;
+ *    Hq % Hkv == 0; chunks must be disjoint, in ascending position order,
+ *    and at most DOCMASK_MAX_CHUNKS.
+ */
+#ifndef DOCMASK_H
+#define DOCMASK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DOCMASK_MAX_CHUNKS 256
+
+/* Global query positions [g_start, g_start + len) held by this rank. */
+typedef struct {
+  int32_t g_start;
+  int32_t len;
+} docmask_chunk;
+
+typedef enum {
+  DOCMASK_OK = 0,
+  DOCMASK_EINVAL = -1,        /* bad argument (null pointer, shape, chunk list, alignment) */
+  DOCMASK_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. D not in {64, 128}) */
+  DOCMASK_EWORKSPACE = -3,    /* workspace missing or smaller than docmask_workspace_size */
+  DOCMASK_EHIP = -4,          /* a HIP launch failed */
+  DOCMASK_EDEVICE_INPUT = -5  /* reported by docmask_check_errors: malformed cu_seqlens */
+} docmask_status;
+
+/* Operations a workspace is sized for. */
+enum { DOCMASK_OP_FWD = 1, DOCMASK_OP_BWD = 2 };
+
+/* Flags of docmask_attn_bwd. */
+enum {
+  /* Add this call's dQ share into dq instead of overwriting it: for split-KV
+   * backward, where each call holds one KV block and the caller sums the
+   * shares (dK and dV of each block are exact per call). */
+  DOCMASK_ACCUMULATE_DQ = 1
+};
+
+/* Workspace bytes docmask_attn_fwd (op = DOCMASK_OP_FWD) or docmask_attn_bwd
+ * (op = DOCMASK_OP_BWD) needs for this problem.  Returns 0 if the arguments
+ * are invalid. */
+size_t docmask_workspace_size(int op, int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks,
+                              int32_t kv_lo, int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d);
+
+/* Tile scheduler (block skipping; production guide "Causal Attention Creates
+ * Rank Load Imbalance"; FlashCP section 3.2 for the need list).
+ * Q tiles of bq rows are anchored at each chunk start and never cross a chunk;
+ * KV tiles of bk keys are anchored at kv_lo; last tiles may be ragged.  A tile
+ * pair is SKIP if it holds no allowed pair, FULL if every pair is allowed,
+ * PARTIAL otherwise.  Outputs (device, int32 unless noted; any may be NULL):
+ *   qtile_desc  [n_qtiles][4]  {kt_lo, kt_full_lo, kt_full_hi, kt_hi}: the
+ *               non-skipped KV tiles [kt_lo, kt_hi) and the FULL ones inside;
+ *               no FULL tile -> kt_full_lo = kt_full_hi = kt_hi; none at all
+ *               -> all four 0.
+ *   kvtile_desc [n_kvtiles][4] {qt_lo, qt_full_lo, qt_full_hi, qt_hi} over the
+ *               global Q-tile index, same encoding.
+ *   need        [n_chunks][2]  key positions [lo, hi) the chunk's rows may
+ *               attend ((0, 0) if none): the chunk's KV need list.
+ *   lpt_q       [n_qtiles]     Q tiles by descending non-skipped KV tile
+ *               count, ties by ascending index.
+ *   lpt_kv      [n_kvtiles]    KV tiles likewise.
+ *   counters    int64 [4]      {non-skipped pairs, FULL, PARTIAL, allowed
+ *               (row, key) pairs per head}.
+ * n_qtiles = sum over chunks of ceil(len / bq); n_kvtiles =
+ * ceil((kv_hi - kv_lo) / bk).  Workspace: docmask_schedule_workspace_size. */
+size_t docmask_schedule_workspace_size(const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
+                                       int32_t kv_hi, int32_t bq, int32_t bk);
+int docmask_schedule(const int32_t* cu_seqlens_dev, int32_t n_docs, const docmask_chunk* chunks,
+                     int32_t n_chunks, int32_t kv_lo, int32_t kv_hi, int32_t bq, int32_t bk,
+                     int32_t* qtile_desc, int32_t* kvtile_desc, int32_t* need, int32_t* lpt_q,
+                     int32_t* lpt_kv, int64_t* counters, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Forward: O (bf16 [Tq][Hq][D]) and LSE (float [Hq][Tq]) of
+ *   O_ih = sum_j softmax_j(scale * q_ih . k_j,h/G) v_j,h/G
+ * over the allowed keys j in [kv_lo, kv_hi) (FlashCP section 2.1).  A call
+ * whose KV range is one block of the sequence yields the partial result that
+ * lse_merge combines. */
+int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                     int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
+                     int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward: exact gradients of <dO, O> (FlashCP Figure 6 "Attention BWD";
+ * the pages do not write it out, so this is the plain calculus):
+ *   P = exp(S - LSE), Delta = rowsum(dO * O), dV = P^T dO,
+ *   dS = P * (dO V^T - Delta), dQ = scale dS K, dK = scale dS^T Q,
+ * summing dK and dV over the query heads of each KV group.  o and lse are the
+ * forward's outputs over the full KV extent of the rows (the merged values
+ * for split-KV).  Outputs are float32: dq [Tq][Hq][D], dk and dv
+ * [Tkv][Hkv][D].  dq is overwritten unless flags has DOCMASK_ACCUMULATE_DQ. */
+int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* d_o, const int32_t* cu_seqlens_dev, int32_t n_docs,
+                     const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo, int32_t kv_hi,
+                     int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float* dq, float* dk,
+                     float* dv, int flags, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Online-softmax merge of partial results over disjoint KV ranges (production
+ * guide, "Core Principle: Split Q, Circulate KV"): per row and head,
+ *   m = max_p LSE_p, LSE = m + ln sum_p exp(LSE_p - m),
+ *   O = sum_p exp(LSE_p - LSE) O_p;  all partials empty -> (0, -inf).
+ * o_parts: bf16 [n_parts][rows][hq][d]; lse_parts: float [n_parts][hq][rows];
+ * o_out: bf16 [rows][hq][d]; lse_out: float [hq][rows].  n_parts >= 1.  Math
+ * in float32.  Outputs must not alias inputs. */
+int lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,
+              int32_t d, void* o_out, float* lse_out, hipStream_t stream);
+
+/* Waits for `stream`, then reports device-side input errors recorded in a
+ * workspace by the last call that used it: DOCMASK_OK or
+ * DOCMASK_EDEVICE_INPUT (cu_seqlens not starting at 0, decreasing, or not
+ * covering the positions used).  After such an error the attention kernels
+ * of that call wrote nothing. */
+int docmask_check_errors(const void* workspace, hipStream_t stream);
+
+/* float32 -> bf16 (round to nearest even) copy of n elements, for callers
+ * that want bf16 gradients. */
+int docmask_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_t stream);
+
+const char* docmask_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DOCMASK_H */

@@ -1,0 +1,38 @@
+"""Helpers shared by the GPU parity tests (device transfer and comparisons)."""
+import numpy as np
+import torch
+
+from document_masked_attention_amd.workloads import bf16_bits_to_f32
+
+O_TOL = 2e-2      # max abs error on O, dQ, dK, dV (bf16 I/O)
+LSE_TOL = 1e-3    # max abs error on the LSE
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> torch.bfloat16 on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def bf16_to_np(t: torch.Tensor) -> np.ndarray:
+    """torch.bfloat16 (any device) -> float64 numpy."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).__lshift__(16) \
+        .view(np.float32).astype(np.float64)
+
+
+def f64(bits: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def assert_close(got, want, tol, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    inf_g, inf_w = np.isinf(got), np.isinf(want)
+    assert np.array_equal(inf_g, inf_w), f"{what}: infinity pattern differs ({inf_g.sum()} vs {inf_w.sum()})"
+    if inf_w.any():
+        assert np.array_equal(got[inf_w], want[inf_w]), f"{what}: infinities of different sign"
+    fin = ~inf_w
+    assert not np.isnan(got).any(), f"{what}: NaN in result"
+    err = np.abs(got[fin] - want[fin]).max() if fin.any() else 0.0
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+    return err

@@ -1,0 +1,101 @@
+"""The C-ABI library on the CPU: it loads, exports every function the public
+header declares, and rejects bad arguments on the host before touching the GPU
+(these calls never reach a HIP launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from document_masked_attention_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "docmask.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.lib_path()):
+        from document_masked_attention_amd import build
+        build.build()
+    return api.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s+\**([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"docmask_attn_fwd", "docmask_attn_bwd", "lse_merge", "docmask_schedule"} <= set(names)
+    handle = ctypes.CDLL(api.lib_path())
+    for n in names:
+        assert hasattr(handle, n), n
+    assert set(names) == set(api._SIGNATURES), "binding and header disagree"
+
+
+FAKE = 0x10000            # an aligned, never dereferenced stand-in address
+MIS = 0x10002             # misaligned
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, n_docs=3, chunks=((0, 100),), kv=(0, 100), hq=4, hkv=2, d=128,
+         scale=0.1, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=16, n_chunks=None):
+    arr, n = api._chunks(list(chunks))
+    return lib.docmask_attn_fwd(q, k, v, cu, n_docs, arr, n if n_chunks is None else n_chunks, kv[0], kv[1], hq,
+                                hkv, d, scale, o, lse, ws, ws_bytes, None)
+
+
+def test_fwd_argument_validation(lib):
+    assert _fwd(lib, d=96) == api.EUNSUPPORTED
+    assert _fwd(lib, hq=6, hkv=4) == api.EINVAL
+    assert _fwd(lib, hkv=0) == api.EINVAL
+    assert _fwd(lib, n_docs=0) == api.EINVAL
+    assert _fwd(lib, cu=None) == api.EINVAL
+    assert _fwd(lib, kv=(50, 10)) == api.EINVAL
+    assert _fwd(lib, kv=(-1, 10)) == api.EINVAL
+    assert _fwd(lib, chunks=((10, 20), (5, 3))) == api.EINVAL          # not ascending
+    assert _fwd(lib, chunks=((10, 20), (25, 3))) == api.EINVAL         # overlapping
+    assert _fwd(lib, chunks=((0, -1),)) == api.EINVAL
+    assert _fwd(lib, n_chunks=api.MAX_CHUNKS + 1) == api.EINVAL
+    assert _fwd(lib, q=MIS) == api.EINVAL
+    assert _fwd(lib, o=None) == api.EINVAL
+    assert _fwd(lib, k=None) == api.EINVAL
+    assert _fwd(lib, scale=float("nan")) == api.EINVAL
+    assert _fwd(lib, ws=None) == api.EWORKSPACE
+    assert _fwd(lib, ws_bytes=16) == api.EWORKSPACE
+    assert _fwd(lib, chunks=()) == api.OK                              # no query rows: nothing to do
+
+
+def test_bwd_and_merge_validation(lib):
+    arr, n = api._chunks([(0, 100)])
+    args = [FAKE] * 7 + [3, arr, n, 0, 100, 4, 2, 128, 0.1, FAKE, FAKE, FAKE]
+    assert lib.docmask_attn_bwd(*args, 0, FAKE, 16, None) == api.EWORKSPACE
+    assert lib.docmask_attn_bwd(*args, 8, FAKE, 1 << 30, None) == api.EINVAL      # unknown flag
+    bad = list(args)
+    bad[16] = MIS                                                                 # misaligned dq
+    assert lib.docmask_attn_bwd(*bad, 0, FAKE, 1 << 30, None) == api.EINVAL
+    assert lib.lse_merge(FAKE, FAKE, 0, 10, 4, 128, FAKE, FAKE, None) == api.EINVAL
+    assert lib.lse_merge(FAKE, FAKE, 2, 10, 4, 32, FAKE, FAKE, None) == api.EUNSUPPORTED
+    assert lib.lse_merge(MIS, FAKE, 2, 10, 4, 128, FAKE, FAKE, None) == api.EINVAL
+    assert lib.lse_merge(FAKE, FAKE, 2, 0, 4, 128, FAKE, FAKE, None) == api.OK
+    assert lib.docmask_f32_to_bf16(FAKE, FAKE, -1, None) == api.EINVAL
+    assert lib.docmask_check_errors(None, None) == api.EINVAL
+
+
+def test_workspace_sizes(lib):
+    fwd = api.workspace_size(api.OP_FWD, 3, [(0, 4096)], 0, 4096, 32, 8, 128)
+    bwd = api.workspace_size(api.OP_BWD, 3, [(0, 4096)], 0, 4096, 32, 8, 128)
+    assert fwd > 0 and bwd > 32 * 4096 * 4                  # the backward holds Delta [Hq, Tq]
+    assert api.workspace_size(api.OP_FWD, 3, [(0, 4096)], 0, 4096, 32, 8, 96) == 0
+    assert api.workspace_size(7, 3, [(0, 4096)], 0, 4096, 32, 8, 128) == 0
+    assert api.schedule_workspace_size([(0, 100)], 0, 100, 16, 16) > 0
+    assert api.schedule_workspace_size([(0, 100)], 0, 100, 0, 16) == 0
+
+
+def test_strerror(lib):
+    for s in (api.OK, api.EINVAL, api.EUNSUPPORTED, api.EWORKSPACE, api.EHIP, api.EDEVICE_INPUT):
+        assert api.strerror(s)
+    assert "unknown" in api.strerror(123)

@@ -1,0 +1,120 @@
+"""Backward kernels on the GPU vs the fp64 oracle (exact gradients).
+
+The GPU backward takes the GPU forward's O and LSE; the oracle uses its own
+float64 forward.  Small problems are compared element by element.  At full
+size, each sampled document is checked through a sub-problem the oracle can
+afford: its last rows as the query chunk against the document's whole key
+range.  dQ of those rows and dK/dV of the keys inside that tail depend only on
+the tail rows (a key is attended only by rows at or after it in its document),
+so the sub-problem's values are exact there."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from document_masked_attention_amd import api
+from document_masked_attention_amd.workloads import custom_workload, make_config, random_lengths, Workload
+from gpu_util import to_dev, bf16_to_np, f64, assert_close, O_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_fwd_bwd(w: Workload, q, k, v, do, accumulate=False):
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    o, lse = api.attn_fwd(qd, kd, vd, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
+    dq, dk, dv = api.attn_bwd(qd, kd, vd, o, lse, dod, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def _check_small(w: Workload, tag):
+    print(f"[bwd] {tag} T={w.total} h={w.hq}/{w.hkv} d={w.d} chunks={w.chunks} kv=[{w.kv_lo},{w.kv_hi})",
+          flush=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    dq, dk, dv = _gpu_fwd_bwd(w, q, k, v, do)
+    wq, wk, wv = oracle.attention_backward(f64(q), f64(k), f64(v), f64(do), w.cu_seqlens, w.chunks, w.kv_lo,
+                                           w.kv_hi, w.scale)
+    assert_close(dq, wq, O_TOL, f"{tag} dQ")
+    assert_close(dk, wk, O_TOL, f"{tag} dK")
+    assert_close(dv, wv, O_TOL, f"{tag} dV")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (8, 1)])
+def test_small_random(d, hq, hkv):
+    rng = np.random.default_rng(2000 + d + 10 * hq + hkv)
+    total = int(rng.integers(300, 600))
+    w = custom_workload(int(rng.integers(1 << 30)), random_lengths(rng, total, 180, p_one=0.1), hq, hkv, d,
+                        backward=True)
+    _check_small(w, f"small d={d} g={hq // hkv}")
+
+
+def test_edge_documents():
+    for lengths in ([1] * 40, [31, 1, 32, 33, 127, 128, 129, 1, 2], [300], [5, 0, 7, 250]):
+        w = custom_workload(len(lengths), lengths, 4, 1, 128, backward=True)
+        _check_small(w, f"edge {lengths[:5]}")
+
+
+def test_chunks_and_kv_ranges():
+    rng = np.random.default_rng(11)
+    for case in range(4):
+        total = int(rng.integers(400, 700))
+        lengths = random_lengths(rng, total, 250)
+        a = int(rng.integers(0, total // 3))
+        b = int(rng.integers(a + 1, total // 2))
+        c = int(rng.integers(total // 2, total - 1))
+        lo = int(rng.integers(0, total // 2))
+        hi = int(rng.integers(lo + 1, total + 1))
+        w = custom_workload(case, lengths, 8, 2, [64, 128][case % 2], chunks=[(a, b - a), (c, total - c)],
+                            kv_lo=lo, kv_hi=hi, backward=True)
+        _check_small(w, f"chunks case {case}")
+
+
+def test_split_kv_backward_sums_to_full():
+    """Per-block calls with the merged O/LSE: exact dK/dV per block, dQ shares add up."""
+    w = custom_workload(21, random_lengths(np.random.default_rng(21), 600, 250), 8, 2, 128, backward=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    cu = w.cu_seqlens
+    o, lse = api.attn_fwd(qd, kd, vd, cu, w.chunks, 0, w.total, w.scale)
+    dq = torch.zeros((w.tq, w.hq, w.d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.total, w.hkv, w.d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    cuts = [0, 128, 129, 333, 600]
+    for x, y in zip(cuts[:-1], cuts[1:]):
+        api.attn_bwd(qd, kd[x:y], vd[x:y], o, lse, dod, cu, w.chunks, x, y, w.scale, dq=dq, dk=dk[x:y],
+                     dv=dv[x:y], accumulate_dq=True)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.attention_backward(f64(q), f64(k), f64(v), f64(do), cu, w.chunks, 0, w.total, w.scale)
+    assert_close(dq.cpu().numpy(), wq, O_TOL, "split dQ")
+    assert_close(dk.cpu().numpy(), wk, O_TOL, "split dK")
+    assert_close(dv.cpu().numpy(), wv, O_TOL, "split dV")
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_full_size_sampled_documents(cfg):
+    w = make_config(cfg)
+    print(f"[bwd] config {cfg}: generating inputs", flush=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    dq, dk, dv = _gpu_fwd_bwd(w, q, k, v, do)
+    cu = w.cu_seqlens
+    lengths = np.diff(cu)
+    order = np.argsort(lengths, kind="stable")
+    docs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1]), int(order[-2])})
+    rng = np.random.default_rng(cfg)
+    g = w.hq // w.hkv
+    for doc in docs:
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        tail = min(b - a, 256)
+        t0 = b - tail
+        kvh = int(rng.integers(w.hkv))
+        heads = np.arange(kvh * g, (kvh + 1) * g)
+        print(f"[bwd] config {cfg} doc {doc} [{a},{b}) tail {tail} kv head {kvh}", flush=True)
+        sq = f64(q[t0:b][:, heads])
+        sdo = f64(do[t0:b][:, heads])
+        sk = f64(k[a:b, kvh:kvh + 1])
+        sv = f64(v[a:b, kvh:kvh + 1])
+        wq, wk, wv = oracle.attention_backward(sq, sk, sv, sdo, cu, [(t0, tail)], a, b, w.scale)
+        assert_close(dq[t0:b][:, heads], wq, O_TOL, f"doc {doc} dQ")
+        assert_close(dk[t0:b, kvh:kvh + 1], wk[t0 - a:], O_TOL, f"doc {doc} dK")
+        assert_close(dv[t0:b, kvh:kvh + 1], wv[t0 - a:], O_TOL, f"doc {doc} dV")

@@ -1,0 +1,166 @@
+"""Forward kernel and LSE merge on the GPU vs the fp64 oracle.
+
+Small problems are compared element by element; the full-size workloads are
+compared on sampled rows that the oracle computes against the full key range
+(their explicit mask over every key), and the 2 x CP rank workload is run the
+way a rank runs it: one partial per (chunk, 8192-key block), merged."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from document_masked_attention_amd import api
+from document_masked_attention_amd.workloads import (custom_workload, make_config, random_lengths,
+                                                     cu_from_lengths, Workload)
+from gpu_util import to_dev, bf16_to_np, f64, assert_close, O_TOL, LSE_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_compare(w: Workload, rows=None, tag=""):
+    print(f"[fwd] {tag} {w.name} seed={w.seed} T={w.total} tq={w.tq} h={w.hq}/{w.hkv} d={w.d} "
+          f"chunks={w.chunks[:4]} kv=[{w.kv_lo},{w.kv_hi})", flush=True)
+    q, k, v = w.q(), w.k(), w.v()
+    o, lse = api.attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
+    torch.cuda.synchronize()
+    o_np = bf16_to_np(o)
+    lse_np = lse.cpu().numpy().astype(np.float64)
+    sel = np.arange(w.tq) if rows is None else np.asarray(rows)
+    want_o, want_l = oracle.attention_forward(f64(q), f64(k), f64(v), w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi,
+                                              w.scale, rows=sel)
+    assert_close(o_np[sel], want_o, O_TOL, f"{tag} O")
+    assert_close(lse_np[:, sel], want_l, LSE_TOL, f"{tag} LSE")
+    return q, k, v, o_np, lse_np
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (8, 2), (8, 1), (16, 2)])
+def test_small_random(d, hq, hkv):
+    rng = np.random.default_rng(1000 + d + 10 * hq + hkv)
+    total = int(rng.integers(300, 700))
+    lengths = random_lengths(rng, total, 200, p_one=0.1)
+    w = custom_workload(int(rng.integers(1 << 30)), lengths, hq, hkv, d)
+    _run_and_compare(w, tag=f"small d={d} g={hq // hkv}")
+
+
+def test_edge_documents():
+    """Length-1 documents, boundaries at tile edges +-1, ragged tails."""
+    for lengths in ([1] * 70, [31, 1, 32, 33, 63, 64, 65, 127, 128, 129, 1, 1, 2],
+                    [64] * 5 + [1], [200], [1, 199], [5, 0, 7, 250]):
+        for hq, hkv in ((4, 1), (8, 8)):
+            w = custom_workload(sum(lengths) + hq, lengths, hq, hkv, 128)
+            _run_and_compare(w, tag=f"edge {lengths[:6]}")
+
+
+def test_whole_sequence_one_document_is_causal():
+    w = custom_workload(77, [1000], 8, 2, 64)
+    _run_and_compare(w, tag="one doc")
+
+
+def test_chunks_and_kv_ranges():
+    """Two-chunk query lists and KV ranges that cut documents, leaving rows empty."""
+    rng = np.random.default_rng(5)
+    for case in range(8):
+        total = int(rng.integers(400, 900))
+        lengths = random_lengths(rng, total, 300)
+        a = int(rng.integers(0, total // 3))
+        b = int(rng.integers(a + 1, total // 2))
+        c = int(rng.integers(total // 2, total - 1))
+        chunks = [(a, b - a), (c, total - c)]
+        lo = int(rng.integers(0, total // 2))
+        hi = int(rng.integers(lo + 1, total + 1))
+        hq, hkv = [(4, 1), (8, 2), (4, 4)][case % 3]
+        w = custom_workload(case, lengths, hq, hkv, [64, 128][case % 2], chunks=chunks, kv_lo=lo, kv_hi=hi)
+        _run_and_compare(w, tag=f"chunks case {case}")
+
+
+def test_first_token_outputs_its_value_row_exactly():
+    lengths = [1, 17, 64, 3, 129, 1, 300]
+    w = custom_workload(9, lengths, 8, 2, 128)
+    q, k, v, o_np, _ = _run_and_compare(w, tag="first token")
+    cu = w.cu_seqlens
+    for a in cu[:-1]:
+        for h in range(8):
+            assert np.array_equal(o_np[a, h], f64(v)[a, h // 4]), f"row {a} head {h}"
+
+
+def test_empty_kv_range_rows():
+    """KV range that no row may attend: O = 0, LSE = -inf everywhere."""
+    w = custom_workload(3, [100, 100], 4, 2, 64, chunks=[(0, 100)], kv_lo=100, kv_hi=200)
+    _, _, _, o_np, lse_np = _run_and_compare(w, tag="empty kv")
+    assert np.all(o_np == 0) and np.all(np.isneginf(lse_np))
+
+
+def test_config1_full():
+    _run_and_compare(make_config(1), tag="config 1")
+
+
+def _sample_rows(w: Workload, n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    cu = w.cu_seqlens
+    pos = w.local_positions()
+    firsts = np.nonzero(np.isin(pos, cu[:-1]))[0][:16]                # first rows of documents
+    ends = np.nonzero(np.isin(pos + 1, cu[1:]))[0][:16]               # last rows of documents
+    edges = np.arange(31, w.tq, 8192)[:8]
+    rand = rng.choice(w.tq, size=n, replace=False)
+    return np.unique(np.concatenate([firsts, ends, edges, rand, [0, w.tq - 1]]))
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_full_size_sampled_rows(cfg):
+    w = make_config(cfg)
+    _run_and_compare(w, rows=_sample_rows(w, 128 if cfg < 5 else 64, cfg), tag=f"config {cfg} sampled")
+
+
+def test_cp_rank_partials_and_merge():
+    """Rank 3 of CP = 8: per-chunk partials over the 8192-key blocks the need
+    list names, merged with lse_merge; sampled rows vs the oracle over the full
+    key range; the merged result also equals the single full-range call."""
+    w = make_config(3)
+    q, k, v = w.q(), w.k(), w.v()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    cu = w.cu_seqlens
+    sched = api.schedule(cu, w.chunks, w.kv_lo, w.kv_hi, 8192, 8192)
+    need = sched["need"].cpu().numpy()
+    row0 = 0
+    for ci, (g, n) in enumerate(w.chunks):
+        lo_b, hi_b = need[ci, 0] // 8192, (need[ci, 1] + 8191) // 8192
+        blocks = list(range(lo_b, hi_b))
+        print(f"[cp] chunk {g} blocks {blocks}", flush=True)
+        parts_o = torch.empty((len(blocks), n, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+        parts_l = torch.empty((len(blocks), w.hq, n), dtype=torch.float32, device="cuda")
+        for i, b in enumerate(blocks):
+            api.attn_fwd(qd[row0:row0 + n], kd[8192 * b:8192 * (b + 1)], vd[8192 * b:8192 * (b + 1)], cu,
+                         [(g, n)], 8192 * b, 8192 * (b + 1), w.scale, out=parts_o[i], lse=parts_l[i])
+        o_m, l_m = api.lse_merge(parts_o, parts_l)
+        o_full, l_full = api.attn_fwd(qd[row0:row0 + n], kd, vd, cu, [(g, n)], w.kv_lo, w.kv_hi, w.scale)
+        torch.cuda.synchronize()
+        o_np, l_np = bf16_to_np(o_m), l_m.cpu().numpy().astype(np.float64)
+        # merged vs single full-range call (both GPU): double rounding of bf16 partials only
+        assert_close(o_np, bf16_to_np(o_full), O_TOL, "merged vs full-range O")
+        assert_close(l_np, l_full.cpu().numpy(), LSE_TOL, "merged vs full-range LSE")
+        rows = np.unique(np.concatenate([np.arange(0, n, 97), [n - 1]]))
+        wq = f64(q[row0 + rows])
+        want_o, want_l = oracle.attention_forward(wq, f64(k), f64(v), cu, [(g + int(r), 1) for r in rows],
+                                                  w.kv_lo, w.kv_hi, w.scale)
+        assert_close(o_np[rows], want_o, O_TOL, f"chunk {g} merged O")
+        assert_close(l_np[:, rows], want_l, LSE_TOL, f"chunk {g} merged LSE")
+        row0 += n
+
+
+def test_merge_against_oracle_small():
+    rng = np.random.default_rng(4)
+    for d in (64, 128):
+        p, rows, hq = 5, 77, 3
+        o = rng.standard_normal((p, rows, hq, d)).astype(np.float32)
+        lse = (3 * rng.standard_normal((p, hq, rows))).astype(np.float32)
+        lse[1, 0, :10] = -np.inf                          # some empty partials
+        lse[:, 1, 20:25] = -np.inf                        # rows with every partial empty
+        o_b = torch.from_numpy(o).to(torch.bfloat16)
+        o_m, l_m = api.lse_merge(o_b.cuda(), torch.from_numpy(lse).cuda())
+        torch.cuda.synchronize()
+        want_o, want_l = oracle.lse_merge(o_b.float().numpy().astype(np.float64), lse.astype(np.float64))
+        assert_close(bf16_to_np(o_m), want_o, O_TOL, "merge O")
+        assert_close(l_m.cpu().numpy(), want_l, LSE_TOL, "merge LSE")
