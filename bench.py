@@ -1,0 +1,294 @@
+"""Benchmark of the document-masked attention hot path on one MI355X.
+
+One step = one pass of the hot path over the 131072-token bimodal packed
+sequence (64 query heads, 8 KV heads, head dim 128): tile scheduler, forward
+(O, LSE), backward preprocess (Delta) and backward (dQ, dK, dV).  The inputs
+are synthetic (seeded normal bf16, the bimodal document-length recipe) and
+already resident in HBM when the timed region starts.
+
+`value` is useful (unmasked) attention TFLOP/s of forward + backward:
+forward 4*D*Hq*pairs, backward 10*D*Hq*pairs (five GEMM-shaped products per
+allowed pair, the QK^T recompute included); pairs = allowed (row, key) pairs
+per head.  The same run also times the forward alone, the backward alone, the
+backward's main kernel alone (the roofline line), the LSE merge of one CP
+rank's per-block partials (2 x CP chunks 3 and 12 of 16 x 8192, lognormal
+documents), and the CPU oracle on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+BWD_PMC_FILE = os.path.join(PROFILE_DIR, "bwd_kernel_T131072_bimodal_h64x8_d128_pmc.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "document_masked_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(per_launch_algo_bytes):
+    """HBM bytes per launch of the backward kernel from the committed counter
+    summary, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(BWD_PMC_FILE):
+        return None
+    vals = {}
+    with open(BWD_PMC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(["bwd.hip", "common.h", "kernels.h"]):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, min_tokens: int = 6144):
+    """The oracle, as it stands, on whole documents covering the first
+    `min_tokens` tokens of the workload, one KV-head group (fwd + bwd)."""
+    import oracle
+    from document_masked_attention_amd.workloads import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cu = w.cu_seqlens
+    end = int(cu[np.searchsorted(cu, min_tokens)])
+    pos = np.arange(end)
+    g = w.hq // w.hkv
+    q = bf16_bits_to_f64(w.q(pos)[:, :g])
+    k = bf16_bits_to_f64(w.k(pos)[:, :1])
+    v = bf16_bits_to_f64(w.v(pos)[:, :1])
+    do = bf16_bits_to_f64(w.do(pos)[:, :g])
+    sub_cu = cu[cu <= end]
+    t0 = time.perf_counter()
+    oracle.attention_backward(q, k, v, do, sub_cu, [(0, end)], 0, end, w.scale)   # runs its own forward
+    dt = time.perf_counter() - t0
+    pairs = oracle.useful_pairs(sub_cu, [(0, end)], 0, end)
+    flops = 14.0 * w.d * g * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fwd+bwd, first {end} tokens ({len(sub_cu) - 1} whole documents), KV head 0 with its "
+                      f"{g} query heads, float64 numpy, {dt:.1f} s",
+            "seconds": round(dt, 2), "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import oracle  # noqa: F401  (imported only for the cpu_baseline leg)
+    from document_masked_attention_amd import api
+    from document_masked_attention_amd.workloads import make_config
+
+    api.lib()                                       # fail loudly if the library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def upload(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ------------------------------------------------------------ workload
+    w = make_config(5)
+    log(f"[bench] workload {w.name}: generating inputs")
+    t0 = time.time()
+    q, k, v, do = upload(w.q()), upload(w.k()), upload(w.v()), upload(w.do())
+    cu = torch.as_tensor(w.cu_seqlens, dtype=torch.int32, device=dev)
+    log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f} s)")
+    sched = api.schedule(cu, w.chunks, w.kv_lo, w.kv_hi, 128, 64)
+    counters = sched["counters"].cpu().numpy()
+    pairs = int(counters[3])
+    fwd_flop = 4.0 * w.d * w.hq * pairs
+    bwd_flop = 10.0 * w.d * w.hq * pairs
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.tq), dtype=torch.float32, device=dev)
+    dq = torch.empty((w.tq, w.hq, w.d), dtype=torch.float32, device=dev)
+    dk = torch.empty((w.tkv, w.hkv, w.d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws_f = torch.empty(api.workspace_size(api.OP_FWD, len(w.lengths), w.chunks, w.kv_lo, w.kv_hi, w.hq, w.hkv, w.d),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(api.workspace_size(api.OP_BWD, len(w.lengths), w.chunks, w.kv_lo, w.kv_hi, w.hq, w.hkv, w.d),
+                       dtype=torch.uint8, device=dev)
+
+    def fwd():
+        api.attn_fwd(q, k, v, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale, out=o, lse=lse, workspace=ws_f)
+
+    def bwd(delta_ready=False):
+        api.attn_bwd(q, k, v, o, lse, do, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale, dq=dq, dk=dk, dv=dv,
+                     accumulate_dq=delta_ready, delta_ready=delta_ready, workspace=ws_b)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n            # ms per call
+
+    for i in range(args.warmup):
+        step()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    if api.check_errors(ws_f) != api.OK or api.check_errors(ws_b) != api.OK:
+        raise RuntimeError("device-side input error")
+    ms_step = timed(step, args.steps)
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step")
+    ms_fwd = timed(fwd, args.steps)
+    ms_bwd = timed(bwd, args.steps)
+    ms_bwd_main = timed(lambda: bwd(delta_ready=True), args.steps)   # scheduler + main backward kernel only
+    log(f"[bench] fwd {ms_fwd:.3f} ms, bwd {ms_bwd:.3f} ms, bwd main kernel {ms_bwd_main:.3f} ms")
+    step()                                            # leave consistent outputs behind
+
+    value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
+    bwd_main_tflops = bwd_flop / (ms_bwd_main * 1e-3) / 1e12
+    algo_bytes = (2 * w.tq * w.hq * w.d * 2 + 2 * w.tkv * w.hkv * w.d * 2 + w.tq * w.hq * 4  # Q, dO, K, V, LSE
+                  + w.tq * w.hq * w.d * 4 + 2 * w.tkv * w.hkv * w.d * 4)                   # dQ, dK, dV
+    traffic = read_traffic(algo_bytes)
+    result = {
+        "metric": "useful attention TFLOP/s fwd & fwd+bwd (% bf16 MFMA peak); merge GB/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq_len": w.total, "documents": len(w.lengths), "seed": w.seed,
+                   "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d, "pairs_per_head": pairs,
+                   "value_is": "fwd+bwd useful TFLOP/s (fwd 4*D*Hq*pairs + bwd 10*D*Hq*pairs)"},
+        "roofline": {"bound": "mfma", "kernel": "bwd_kernel<128>",
+                     "achieved": round(bwd_main_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_main_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes": int(algo_bytes),
+                     "launch_ms": round(ms_bwd_main, 4)},
+        "components": {
+            "fwd": {"ms": round(ms_fwd, 4), "tflops": round(fwd_flop / (ms_fwd * 1e-3) / 1e12, 3),
+                    "frac_of_peak": round(fwd_flop / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "bwd": {"ms": round(ms_bwd, 4), "tflops": round(bwd_flop / (ms_bwd * 1e-3) / 1e12, 3),
+                    "frac_of_peak": round(bwd_flop / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "tflops_8d_count": round(0.8 * bwd_flop / (ms_bwd * 1e-3) / 1e12, 3)},
+            "scheduler_counters": {"nonskip_tiles_128x64": int(counters[0]), "full": int(counters[1]),
+                                   "partial": int(counters[2])},
+        },
+    }
+    del o, lse, dq, dk, dv, q, k, v, do, ws_f, ws_b
+    torch.cuda.empty_cache()
+
+    if not args.no_merge:
+        result["components"]["merge"] = bench_merge(api, torch, dev, upload, args.steps)
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": a.numel() * 4, "write": a.numel() * 4}
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+        log(f"[bench] cpu baseline {result['cpu_baseline']['seconds']} s")
+    print(json.dumps(result), flush=True)
+
+
+def bench_merge(api, torch, dev, upload, steps):
+    """lse_merge of rank 3's per-block partials (CP = 8, chunks 3 and 12)."""
+    from document_masked_attention_amd.workloads import make_config
+    w = make_config(3)
+    log(f"[bench] merge workload {w.name}: generating inputs")
+    q, k, v = upload(w.q()), upload(w.k()), upload(w.v())
+    cu = torch.as_tensor(w.cu_seqlens, dtype=torch.int32, device=dev)
+    need = api.schedule(cu, w.chunks, w.kv_lo, w.kv_hi, 8192, 8192)["need"].cpu().numpy()
+    blk = w.kv_block
+    jobs = []
+    row0 = 0
+    total_bytes = 0.0
+    dense_bytes = 0.0
+    for ci, (g, n) in enumerate(w.chunks):
+        blocks = list(range(need[ci, 0] // blk, (need[ci, 1] + blk - 1) // blk))
+        po = torch.empty((len(blocks), n, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        pl = torch.empty((len(blocks), w.hq, n), dtype=torch.float32, device=dev)
+        for i, b in enumerate(blocks):
+            api.attn_fwd(q[row0:row0 + n], k[blk * b:blk * (b + 1)], v[blk * b:blk * (b + 1)], cu, [(g, n)],
+                         blk * b, blk * (b + 1), w.scale, out=po[i], lse=pl[i])
+        oo = torch.empty((n, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        lo = torch.empty((w.hq, n), dtype=torch.float32, device=dev)
+        finite = int(torch.isfinite(pl).sum().item())
+        p_c = len(blocks)
+        total_bytes += p_c * n * w.hq * 4 + finite * 2 * w.d + n * w.hq * (2 * w.d + 4)
+        dense_bytes += p_c * n * w.hq * (4 + 2 * w.d) + n * w.hq * (2 * w.d + 4)
+        jobs.append((po, pl, oo, lo))
+        row0 += n
+    torch.cuda.synchronize()
+
+    def merge_all():
+        for po, pl, oo, lo in jobs:
+            api.lse_merge(po, pl, o_out=oo, lse_out=lo)
+
+    merge_all()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(max(steps, 10)):
+        merge_all()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(steps, 10)
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    parts = [j[0].shape[0] for j in jobs]
+    return {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
+            "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "bound": "hbm"}
+
+
+if __name__ == "__main__":
+    main()

@@ -19,6 +19,7 @@ _lib = None
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE_INPUT = 0, -1, -2, -3, -4, -5
 OP_FWD, OP_BWD = 1, 2
 ACCUMULATE_DQ = 1
+DELTA_READY = 2
 MAX_CHUNKS = 256
 
 _vp = ctypes.c_void_p
@@ -179,8 +180,11 @@ def attn_fwd(q, k, v, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float |
 
 
 def attn_bwd(q, k, v, o, lse, d_o, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float | None = None,
-             dq=None, dk=None, dv=None, accumulate_dq: bool = False, workspace=None):
-    """float32 dQ [Tq, Hq, D], dK and dV [Tkv, Hkv, D]."""
+             dq=None, dk=None, dv=None, accumulate_dq: bool = False, delta_ready: bool = False, workspace=None):
+    """float32 dQ [Tq, Hq, D], dK and dV [Tkv, Hkv, D].
+
+    ``delta_ready`` requires ``workspace`` from an earlier call with the same
+    o, d_o, chunks and heads."""
     q, k, v, o, d_o = _bits(q), _bits(k), _bits(v), _bits(o), _bits(d_o)
     tq, hq, d = q.shape
     tkv, hkv, _ = k.shape
@@ -197,11 +201,14 @@ def attn_bwd(q, k, v, o, lse, d_o, cu_seqlens, chunks, kv_lo: int, kv_hi: int, s
     if ws_bytes == 0:
         raise DocmaskError(EINVAL, "docmask_workspace_size")
     if workspace is None or workspace.numel() < ws_bytes:
+        if delta_ready:
+            raise ValueError("delta_ready needs the workspace of an earlier call")
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     arr, n = _chunks(chunks)
     st = lib().docmask_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(cu), n_docs, arr, n,
                                 kv_lo, kv_hi, hq, hkv, d, float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
-                                ACCUMULATE_DQ if accumulate_dq else 0, _ptr(workspace), workspace.numel(),
+                                (ACCUMULATE_DQ if accumulate_dq else 0) | (DELTA_READY if delta_ready else 0),
+                                _ptr(workspace), workspace.numel(),
                                 _stream())
     _check(st, "docmask_attn_bwd")
     return dq, dk, dv

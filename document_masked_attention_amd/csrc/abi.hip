@@ -225,7 +225,7 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   int st = check_shape(n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, &pr);
   if (st != DOCMASK_OK) return st;
   if (!cu_seqlens_dev || !std::isfinite(softmax_scale)) return DOCMASK_EINVAL;
-  if (flags & ~DOCMASK_ACCUMULATE_DQ) return DOCMASK_EINVAL;
+  if (flags & ~(DOCMASK_ACCUMULATE_DQ | DOCMASK_DELTA_READY)) return DOCMASK_EINVAL;
   if (pr.tq > 0 && (!q || !o || !lse || !d_o || !dq || !aligned16(q) || !aligned16(o) || !aligned16(d_o) ||
                     !aligned16(dq) || !aligned4(lse)))
     return DOCMASK_EINVAL;
@@ -270,7 +270,8 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   bp.tq = (int32_t)pr.tq; bp.xcd_cluster = kXcdCluster;
   bp.scale = softmax_scale;
   bp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-  return hip_status(launch_bwd(bp, d, (flags & DOCMASK_ACCUMULATE_DQ) != 0, stream));
+  return hip_status(launch_bwd(bp, d, (flags & DOCMASK_ACCUMULATE_DQ) != 0, (flags & DOCMASK_DELTA_READY) != 0,
+                               stream));
 }
 
 int lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,

@@ -324,14 +324,14 @@ hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, bool delta_ready, hipStream_t stream) {
   hipError_t e;
   if (!accumulate_dq) {
     e = launch_fill_zero(p.dq, (int64_t)p.tq * p.hq * d, stream);
     if (e != hipSuccess) return e;
   }
   const long long rh_threads = (long long)p.tq * p.hq * (d / 8);
-  if (rh_threads > 0) {
+  if (rh_threads > 0 && !delta_ready) {
     const long long blocks = (rh_threads + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (d == 128)

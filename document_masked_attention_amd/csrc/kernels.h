@@ -75,6 +75,6 @@ int fwd_rows_per_tile(int group);
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
 hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, bool delta_ready, hipStream_t stream);
 
 }  // namespace docmask

@@ -77,7 +77,11 @@ enum {
   /* Add this call's dQ share into dq instead of overwriting it: for split-KV
    * backward, where each call holds one KV block and the caller sums the
    * shares (dK and dV of each block are exact per call). */
-  DOCMASK_ACCUMULATE_DQ = 1
+  DOCMASK_ACCUMULATE_DQ = 1,
+  /* The workspace already holds Delta = rowsum(dO * O) from an earlier call
+   * with the same o, d_o, chunks and heads (e.g. the previous KV block of a
+   * split-KV backward): skip recomputing it. */
+  DOCMASK_DELTA_READY = 2
 };
 
 /* Workspace bytes docmask_attn_fwd (op = DOCMASK_OP_FWD) or docmask_attn_bwd
@@ -132,7 +136,8 @@ int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
  * summing dK and dV over the query heads of each KV group.  o and lse are the
  * forward's outputs over the full KV extent of the rows (the merged values
  * for split-KV).  Outputs are float32: dq [Tq][Hq][D], dk and dv
- * [Tkv][Hkv][D].  dq is overwritten unless flags has DOCMASK_ACCUMULATE_DQ. */
+ * [Tkv][Hkv][D].  dq is overwritten unless flags has DOCMASK_ACCUMULATE_DQ;
+ * Delta is recomputed unless flags has DOCMASK_DELTA_READY. */
 int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* d_o, const int32_t* cu_seqlens_dev, int32_t n_docs,
                      const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo, int32_t kv_hi,
