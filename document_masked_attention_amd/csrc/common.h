@@ -75,4 +75,36 @@ __device__ __forceinline__ float wave_shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over the lane pair (l, l ^ 32) with v_permlane32_swap: the
+// swap leaves {x_l, x_(l^32)} in the two results of every lane.
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, output lane i gets element e (0..3) = the 16-bit value at
+// (address supplied by lane 4e + i/4 of the group) + (i mod 4) elements.  So a
+// lane that supplies the address of row R, column C of a row-major tile feeds
+// row R's columns C..C+3 to four lanes; MFMA operands whose contraction index
+// runs down the rows of a tile are read straight from the row-major tile.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+}
+
+// Two transpose reads assembled into one 8 x bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p0, const uint16_t* p1) {
+  const v4i16 a = lds_read_tr16(p0);
+  const v4i16 b = lds_read_tr16(p1);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
 }  // namespace docmask

@@ -20,33 +20,35 @@
 // With keys on the accumulator rows, a query's scores sit in one lane pair
 // (lane and lane^32), so row max/sum are in-register plus one cross-half swap.
 // The accumulator row order of S^T is {0-3, 8-11 | 4-7, 12-15} per 16 keys for
-// the two lane halves; V^T is stored in LDS in that same permuted key order so
-// each lane fetches its 8 keys with one 16-byte read.
+// the two lane halves; the V^T operand is gathered in that same key order from
+// the row-major V tile with LDS transpose reads (ds_read_b64_tr_b16).
+// K/V tiles are double-buffered in LDS with one barrier per tile; the MFMAs of
+// the next tile's S^T are issued before the current tile's softmax.
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace docmask {
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-// Position (in units of 4 keys) of key group kg inside a 64-key V^T row: the
-// two middle 4-key blocks of every 16 keys are swapped.
-__device__ __forceinline__ int vt_pos4(int kg) { return (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1); }
+// Rescale threshold (log2 units): the running row maximum used as the softmax
+// reference is only raised when a tile's maximum exceeds it by more than this,
+// so exp2 arguments stay <= kRescaleTau and most tiles skip the O rescale.
+// The result is the same after the final normalisation by the row sum.
+constexpr float kRescaleTau = 8.f;
 
 template <int D, int RB, int HB>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   static_assert(RB * HB == 4, "four waves per workgroup");
   constexpr int BK = kFwdBK;
-  constexpr int KSTR = D + 8;           // K row stride in LDS (bf16 elements)
-  constexpr int VSTR = BK + 8;          // V^T row stride
+  constexpr int KSTR = D + 8;           // K row stride (bf16): 16-byte row reads hit distinct banks
+  constexpr int VSTR = D + 32;          // V row stride: transpose reads of 4 rows hit distinct banks
   constexpr int CPK = D / 8;            // 16-byte chunks per key row
   constexpr int KPP = 256 / CPK;        // keys per load pass
   constexpr int KPASS = BK / KPP;
-  constexpr int VUNITS = 16 * CPK;      // (4 keys x 8 d) units per V tile
   constexpr int NKS = D / 16;           // k-steps of QK^T
   constexpr int NDB = D / 32;           // 32-wide d blocks of O
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BK * VSTR];
 
   if (p.err[0]) return;
 
@@ -68,8 +70,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int qr = 32 * rb + ln;
   const bool row_ok = qr < nrows;
   const int gi = g_row0 + qr;
-  const int dsi = row_ok ? doc_start(p.cu, p.n_docs, gi) : 0;
   const size_t o_off = ((size_t)(l_row0 + qr) * p.hq + head) * D;
+  // allowed keys of this row: [a_lo, a_lo + a_w] (global positions); empty rows never match
+  int a_lo = 0x40000000, a_w = 0;
+  if (row_ok) {
+    const int lo = max(doc_start(p.cu, p.n_docs, gi), p.kv_lo), hi = min(gi, p.kv_hi - 1);
+    if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
+  }
 
   // Q operand of this lane: row qr, d = 16 s + 8 hh .. +8, for every k-step s.
   bf16x8 qf[NKS];
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   f32x16 oacc[NDB];
 #pragma unroll
   for (int b = 0; b < NDB; ++b) oacc[b] = f32x16{};
-  float m_run = -INFINITY;   // running max of scale*log2(e)*s
+  float m_run = -INFINITY;   // softmax reference (scale*log2(e) units)
   float l_run = 0.f;         // this lane half's share of the exp-sum
 
   const int tkv = p.kv_hi - p.kv_lo;
@@ -90,125 +97,138 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
 
-  // global -> register staging of one K/V tile
-  uint4 kreg[KPASS];
-  uint4 vreg[4];
+  // global -> register -> LDS staging of K and V tiles (row-major, 16-byte
+  // chunks).  Padding keys of a ragged last tile load the last real row
+  // instead: their scores are always masked (P = 0 exactly), so any finite
+  // K/V row will do.
   const int kc = tid % CPK, kk0 = tid / CPK;
-  const int vkg = tid & 15, vc = tid >> 4;
-  auto load_tile = [&](int kt) {
-    const int key0 = kt * BK;
+  auto load_rows = [&](const uint16_t* base, int kt, uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < KPASS; ++pp) {
-      const int key = key0 + kk0 + KPP * pp;
-      kreg[pp] = key < tkv ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * kv_rstride + 8 * kc)
-                           : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < VUNITS) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 4 * vkg + i;
-        vreg[i] = key < tkv ? *reinterpret_cast<const uint4*>(vbase + (size_t)key * kv_rstride + 8 * vc)
-                            : make_uint4(0, 0, 0, 0);
-      }
+      const int key = min(kt * BK + kk0 + KPP * pp, tkv - 1);
+      reg[pp] = *reinterpret_cast<const uint4*>(base + (size_t)key * kv_rstride + 8 * kc);
     }
   };
-  auto store_tile = [&]() {
+  auto store_rows = [&](uint16_t* lds, int stride, const uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < KPASS; ++pp)
-      *reinterpret_cast<uint4*>(&k_lds[(kk0 + KPP * pp) * KSTR + 8 * kc]) = kreg[pp];
-    if (tid < VUNITS) {
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-      const int col = 4 * vt_pos4(vkg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint2 val;
-        if (e & 1) { val.x = pack_hi(w0[wd], w1[wd]); val.y = pack_hi(w2[wd], w3[wd]); }
-        else       { val.x = pack_lo(w0[wd], w1[wd]); val.y = pack_lo(w2[wd], w3[wd]); }
-        *reinterpret_cast<uint2*>(&vt_lds[(8 * vc + e) * VSTR + col]) = val;
-      }
-    }
+      *reinterpret_cast<uint4*>(&lds[(kk0 + KPP * pp) * stride + 8 * kc]) = reg[pp];
   };
+  // transpose-read source address of this lane inside a V tile (see lds_read_tr16)
+  const int i16 = lane & 15;
+  const int vt_off = (4 * hh + (i16 >> 2)) * VSTR + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
 
-  if (kt_lo < kt_hi) load_tile(kt_lo);
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    __syncthreads();                 // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < kt_hi) load_tile(kt + 1);
-
-    // S^T = K Q^T for the two 32-key blocks of the tile
-    f32x16 sacc[2];
+  // S^T = K Q^T for the two 32-key blocks of the tile held in K buffer kb_
+  auto compute_s = [&](const uint16_t* kl, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(32 * kb + ln) * KSTR + 16 * s + 8 * hh]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&kl[(32 * kb + ln) * KSTR + 16 * s + 8 * hh]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
       }
     }
+  };
+
+  // Software pipeline over the n tiles (index u = kt - kt_lo): K tile u lives in
+  // k_lds[u & 1] and V tile u in v_lds[u & 1].  Iteration u issues the MFMAs of
+  // S(u + 1) before the softmax of tile u so the matrix cores run while the
+  // VALU works; K is therefore staged two tiles ahead and V one tile ahead.
+  const int n = kt_hi - kt_lo;
+  f32x16 s_cur[2], s_nxt[2];
+  if (n > 0) {
+    uint4 kr0[KPASS], vr0[KPASS], kr1[KPASS];
+    load_rows(kbase, kt_lo, kr0);
+    load_rows(vbase, kt_lo, vr0);
+    load_rows(kbase, min(kt_lo + 1, kt_hi - 1), kr1);
+    store_rows(k_lds[0], KSTR, kr0);
+    store_rows(v_lds[0], VSTR, vr0);
+    store_rows(k_lds[1], KSTR, kr1);
+    __syncthreads();
+    compute_s(k_lds[0], s_cur);
+    __syncthreads();                  // every wave has read K tile 0 before it is overwritten
+  }
+  // One pipeline step; `has_next` is a compile-time flag so that the steady-state
+  // body has no branches between the next tile's MFMAs and this tile's softmax.
+  auto step = [&](int u, auto has_next_c) __attribute__((always_inline)) {
+    constexpr bool has_next = decltype(has_next_c)::value;
+    const int kt = kt_lo + u;
+    uint4 kreg[KPASS], vreg[KPASS];
+    if (has_next) {
+      load_rows(kbase, min(kt + 2, kt_hi - 1), kreg);   // in flight during this tile's math
+      load_rows(vbase, kt + 1, vreg);
+      compute_s(k_lds[(u + 1) & 1], s_nxt);
+    }
+
     // document mask on PARTIAL tiles and on the ragged last tile (its padding
     // keys lie beyond kv_hi even when every real pair is allowed)
     if (kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv) {
-      const int key0 = p.kv_lo + kt * BK + 4 * hh;
+      const int rel0 = p.kv_lo + kt * BK + 4 * hh - a_lo;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = key0 + 32 * kb + 8 * (r >> 2) + (r & 3);
-          const bool ok = (j >= dsi) && (j <= gi) && (j < p.kv_hi);
-          if (!ok) sacc[kb][r] = -INFINITY;
+          const unsigned rel = (unsigned)(rel0 + 32 * kb + 8 * (r >> 2) + (r & 3));
+          if (rel > (unsigned)a_w) s_cur[kb][r] = -INFINITY;
         }
     }
-    // online softmax (base 2)
+    // online softmax (base 2) with a lazily raised reference
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, wave_shfl_xor32(mx));
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
+    mx = pair_max32(mx);
+    const float m_tile = mx * p.scale_log2;
+    if (__any(m_tile > m_run + kRescaleTau)) {       // wave-uniform branch
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rs = 0.f;
+    bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_use));
-        sacc[kb][r] = e;
-        rs += e;
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], p.scale_log2, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r + 1], p.scale_log2, -m_use));
+        rs += e0 + e1;
+        const bf16x2 two = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
+        pf[2 * kb + (r >> 3)][r & 7] = two[0];
+        pf[2 * kb + (r >> 3)][(r & 7) + 1] = two[1];
       }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+    l_run += rs;
 
-    // O^T += V^T P^T, 16 keys per step
+    // O^T += V^T P^T, 16 keys per step; V^T comes from the row-major V tile
+    // through transpose reads, in the accumulator's permuted key order
+    const uint16_t* vl = v_lds[u & 1];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kb = s >> 1, base = 8 * (s & 1);
-      bf16x8 pf;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const bf16x2 two = __builtin_convertvector(f32x2{sacc[kb][base + i], sacc[kb][base + i + 1]}, bf16x2);
-        pf[i] = two[0];
-        pf[i + 1] = two[1];
-      }
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int b = 0; b < NDB; ++b) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt_lds[(32 * b + ln) * VSTR + 16 * s + 8 * hh]);
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[b], 0, 0, 0);
+        const uint16_t* vp = vl + vt_off + 16 * s * VSTR + 32 * b;
+        const bf16x8 vf = tr_operand(vp, vp + 8 * VSTR);
+        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[b], 0, 0, 0);
       }
+    if (has_next) {
+      store_rows(k_lds[u & 1], KSTR, kreg);         // K tile u + 2 (the last tile again near the end)
+      store_rows(v_lds[(u + 1) & 1], VSTR, vreg);
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     }
-  }
+  };
+  for (int u = 0; u + 1 < n; ++u) step(u, std::true_type{});
+  if (n > 0) step(n - 1, std::false_type{});
 
   // epilogue: normalise, write O (bf16) and LSE (natural log)
-  const float l_tot = l_run + wave_shfl_xor32(l_run);
+  const float l_tot = pair_sum32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
 #pragma unroll
