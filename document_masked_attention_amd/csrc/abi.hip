@@ -69,8 +69,9 @@ ChunkTable make_table(const docmask_chunk* chunks, int32_t n_chunks) {
 
 // Workspace layout of one entry point (byte offsets; 0 = region absent).
 struct Layout {
-  size_t plan_q = 0, key_q = 0, lpt_q = 0, kvdesc = 0, key_kv = 0, lpt_kv = 0, hist = 0, delta = 0, total = 0;
-  int64_t n_qt = 0, n_kt = 0;
+  size_t plan_q = 0, key_q = 0, lpt_q = 0, kvdesc = 0, key_kv = 0, lpt_kv = 0, plan_q2 = 0, hist = 0, delta = 0,
+         total = 0;
+  int64_t n_qt = 0, n_kt = 0, n_qt2 = 0, n_kt2 = 0;
 };
 
 Layout fwd_layout(const docmask_chunk* chunks, int32_t n_chunks, const Problem& pr) {
@@ -88,15 +89,22 @@ Layout fwd_layout(const docmask_chunk* chunks, int32_t n_chunks, const Problem& 
 }
 
 Layout bwd_layout(const docmask_chunk* chunks, int32_t n_chunks, const Problem& pr, int32_t hq) {
+  // dK/dV pass: 32-row query blocks x 128-key tiles; dQ pass: forward-style tiles
   Layout L;
   L.n_qt = count_qtiles(chunks, n_chunks, kBwdBQ);
   L.n_kt = (pr.tkv + (int64_t)kBwdBK - 1) / kBwdBK;
+  L.n_qt2 = count_qtiles(chunks, n_chunks, dq_rows_per_tile(pr.group));
+  L.n_kt2 = (pr.tkv + (int64_t)kDqBK - 1) / kDqBK;
   size_t off = kAlign;
   L.plan_q = off; off = align_up(off + (size_t)L.n_qt * QP_WORDS * 4);
   L.kvdesc = off; off = align_up(off + (size_t)L.n_kt * 4 * 4);
   L.key_kv = off; off = align_up(off + (size_t)L.n_kt * 4);
   L.lpt_kv = off; off = align_up(off + (size_t)L.n_kt * 4);
-  L.hist = off;   off = align_up(off + (size_t)(L.n_qt + 1) * 4);
+  L.plan_q2 = off; off = align_up(off + (size_t)L.n_qt2 * QP_WORDS * 4);
+  L.key_q = off;  off = align_up(off + (size_t)L.n_qt2 * 4);
+  L.lpt_q = off;  off = align_up(off + (size_t)L.n_qt2 * 4);
+  const int64_t hist_n = (L.n_qt > L.n_kt2 ? L.n_qt : L.n_kt2) + 1;
+  L.hist = off;   off = align_up(off + (size_t)hist_n * 4);
   L.delta = off;  off = align_up(off + (size_t)hq * pr.tq * 4);
   L.total = off;
   return L;
@@ -236,6 +244,7 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   if (!workspace || workspace_bytes < L.total) return DOCMASK_EWORKSPACE;
   if (!aligned16(workspace)) return DOCMASK_EINVAL;
 
+  // schedule of the dK/dV pass (KV-tile ranges, LPT over KV tiles)
   SchedParams sp;
   std::memset(&sp, 0, sizeof(sp));
   sp.ch = make_table(chunks, n_chunks);
@@ -249,6 +258,17 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   int32_t* lpt_kv = at<int32_t>(workspace, L.lpt_kv);
   hipError_t e = launch_schedule(sp, nullptr, lpt_kv, at<int32_t>(workspace, L.hist), stream);
   if (e != hipSuccess) return DOCMASK_EHIP;
+  // schedule of the dQ pass (forward-style Q-tile ranges, LPT over Q tiles)
+  SchedParams sq = sp;
+  sq.bq = dq_rows_per_tile(pr.group); sq.bk = kDqBK;
+  sq.n_qtiles = (int32_t)L.n_qt2; sq.n_kvtiles = (int32_t)L.n_kt2;
+  sq.plan_q = at<int32_t>(workspace, L.plan_q2);
+  sq.kvdesc = nullptr;
+  sq.key_kv = nullptr;
+  sq.key_q = at<int32_t>(workspace, L.key_q);
+  int32_t* lpt_q = at<int32_t>(workspace, L.lpt_q);
+  e = launch_schedule(sq, lpt_q, nullptr, at<int32_t>(workspace, L.hist), stream);
+  if (e != hipSuccess) return DOCMASK_EHIP;
 
   BwdParams bp;
   std::memset(&bp, 0, sizeof(bp));
@@ -261,17 +281,20 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   bp.dq = dq; bp.dk = dk; bp.dv = dv;
   bp.delta = at<float>(workspace, L.delta);
   bp.cu = cu_seqlens_dev;
-  bp.plan_q = sp.plan_q;
+  bp.plan_kq = sp.plan_q;
   bp.kvdesc = sp.kvdesc;
   bp.lpt_kv = lpt_kv;
+  bp.plan_q = sq.plan_q;
+  bp.lpt_q = lpt_q;
   bp.err = sp.err;
   bp.n_docs = n_docs; bp.n_qtiles = (int32_t)L.n_qt; bp.n_kvtiles = (int32_t)L.n_kt;
+  bp.n_qtiles_dq = (int32_t)L.n_qt2;
   bp.hq = hq; bp.hkv = hkv; bp.group = pr.group; bp.kv_lo = kv_lo; bp.kv_hi = kv_hi;
   bp.tq = (int32_t)pr.tq; bp.xcd_cluster = kXcdCluster;
+  bp.accumulate_dq = (flags & DOCMASK_ACCUMULATE_DQ) != 0;
   bp.scale = softmax_scale;
   bp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-  return hip_status(launch_bwd(bp, d, (flags & DOCMASK_ACCUMULATE_DQ) != 0, (flags & DOCMASK_DELTA_READY) != 0,
-                               stream));
+  return hip_status(launch_bwd(bp, d, (flags & DOCMASK_DELTA_READY) != 0, stream));
 }
 
 int lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,

@@ -8,28 +8,25 @@
 //   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 // with dK and dV summed over the query heads of each KV group.
 //
-// Work item = (KV tile of 128 keys, KV head); 4 waves, wave w owns keys
-// 32w..32w+31 and keeps their K and V rows, dK and dV in registers.  The item
-// walks the query tiles (32 rows) that attend its keys -- the scheduler's
-// per-KV-tile range -- for every query head of the group, recomputing P from
-// the LSE.  MFMA layouts (v_mfma_f32_32x32x16_bf16):
-//   S   [q][key]  = Q K^T    (A = Q rows from LDS, B = K in registers)
-//   dV^T[d][key] += dO^T P   (A = dO^T from LDS, B = P from the S accumulators)
-//   dP  [q][key]  = dO V^T   (A = dO rows from LDS, B = V in registers)
-//   dK^T[d][key] += Q^T dS   (A = Q^T from LDS, B = dS from registers)
-//   dQ  [q][d]    = dS K     (A = dS staged in LDS, B = K^T from LDS), added to
-//                            the float32 dQ with atomics (several KV tiles
-//                            contribute to one query row).
-// Accumulator rows of S are ordered {0-3, 8-11 | 4-7, 12-15} per 16 queries
-// for the two lane halves; Q^T and dO^T are stored in that permuted query
-// order so each lane reads its 8 queries with one 16-byte load.
+// Two kernels, both deterministic (no atomics):
+//
+// * dkdv_kernel, key-major.  Work item = (KV tile of 128 keys, KV head);
+//   8 waves x 16 keys, each wave keeping its K and V rows (MFMA B operands)
+//   and its dK, dV accumulators in registers.  It walks every (32-row query
+//   block, query head of the group) that attends the tile -- the scheduler's
+//   per-KV-tile range -- with the Q and dO rows double-buffered in LDS:
+//     S = Q K^T,  P = exp2(S c - LSE2),  dV^T += dO^T P,
+//     dP = dO V^T,  dS = P (dP - Delta),  dK^T += Q^T dS
+//   (v_mfma_f32_16x16x32_bf16; Q^T and dO^T come from the row-major tiles
+//   through LDS transpose reads).
+// * dq_kernel, query-major, shaped like the forward.  Work item = (query tile,
+//   KV head, block of query heads), 8 waves; each wave owns 32 rows x 1 head
+//   and walks the tile's KV range:
+//     S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T
+//   (v_mfma_f32_32x32x16_bf16; K^T through transpose reads).
 #include "kernels.h"
 
 namespace docmask {
-
-__device__ __forceinline__ uint32_t bpack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t bpack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-__device__ __forceinline__ int perm_pos4(int g) { return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1); }
 
 // Delta = rowsum(dO * O) per (row, head), float32 from the bf16 inputs.
 template <int D>
@@ -60,35 +57,28 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ dst, int64_t n) {
-  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (i0 + 4 <= n) *reinterpret_cast<float4*>(dst + i0) = make_float4(0.f, 0.f, 0.f, 0.f);
-  else
-    for (int64_t i = i0; i < n; ++i) dst[i] = 0.f;
+__device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float b0, float b1, float b2,
+                                      float b3) {
+  const bf16x2 p0 = __builtin_convertvector(f32x2{a0, a1}, bf16x2);
+  const bf16x2 p1 = __builtin_convertvector(f32x2{a2, a3}, bf16x2);
+  const bf16x2 p2 = __builtin_convertvector(f32x2{b0, b1}, bf16x2);
+  const bf16x2 p3 = __builtin_convertvector(f32x2{b2, b3}, bf16x2);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// ------------------------------------------------------------------ dK, dV
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   constexpr int BQ = kBwdBQ;            // 32 query rows per step
-  constexpr int BK = kBwdBK;            // 128 keys per work item
-  constexpr int NKS = D / 16;           // k-steps over d
-  constexpr int NDB = D / 32;           // 32-wide d blocks
-  constexpr int CPK = D / 8;            // 16-byte chunks per row
-  constexpr int RSTR = D + 8;           // row-major Q / dO stride (bf16)
-  constexpr int TSTR = BQ + 8;          // Q^T / dO^T stride
-  constexpr int SSTR = BK + 8;          // dS stride
-  constexpr int KTSTR = BK + 8;         // K^T stride
-  constexpr int QUNITS = (BQ / 4) * CPK;   // (4 rows x 8 d) units of one 32-row block
-  constexpr int WPD = 4 / NDB;          // waves per d block in the dQ step
-  constexpr int KPW = BK / WPD;         // keys each wave sums in the dQ step
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[BQ * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[BQ * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[BQ * SSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * KTSTR];
-  __shared__ float lse_lds[BQ], delta_lds[BQ];
-  __shared__ int32_t dstart_lds[BQ];
+  constexpr int BK = kBwdBK;            // 128 keys per work item, 16 per wave
+  constexpr int NKS = D / 32;           // k-steps over d (16x16x32)
+  constexpr int NDB = D / 16;           // 16-wide d blocks of dK^T / dV^T
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int QS = D + 8;             // row stride of the Q / dO tiles (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t q_s[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t do_s[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dlt_s[2][BQ];
 
   if (p.err[0]) return;
 
@@ -100,236 +90,340 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const int qt_lo = kd[0], qt_flo = kd[1], qt_fhi = kd[2], qt_hi = kd[3];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, i16 = lane & 15;
   const int tkv = p.kv_hi - p.kv_lo;
-  const int key_l = tile * BK + 32 * wave + ln;     // this lane's key, local KV row
+  const int key_l = tile * BK + 16 * wave + i16;    // this lane's key (local KV row)
   const bool key_ok = key_l < tkv;
   const int key_g = p.kv_lo + key_l;
+  // rows that may attend this key: key_g <= i < end of its document
+  const int key_end = key_ok ? doc_end(p.cu, p.n_docs, key_g) : key_g;
   const size_t kv_rstride = (size_t)p.hkv * D;
+  const bool ragged = (tile + 1) * BK > tkv;
 
-  // K and V rows of this lane's key as MFMA B operands (d = 16 s + 8 hh ..)
+  // K and V rows of this lane's key as MFMA B operands: d = 32 s + 8 g .. +8
   bf16x8 kf[NKS], vf[NKS];
   {
-    const uint16_t* kr = p.k + (size_t)key_l * kv_rstride + (size_t)kvh * D + 8 * hh;
-    const uint16_t* vr = p.v + (size_t)key_l * kv_rstride + (size_t)kvh * D + 8 * hh;
+    const int kl = min(key_l, tkv - 1);               // padding keys: any finite row, masked below
+    const uint16_t* kr = p.k + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * g;
+    const uint16_t* vr = p.v + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      kf[s] = key_ok ? *reinterpret_cast<const bf16x8*>(kr + 16 * s) : bf16x8{};
-      vf[s] = key_ok ? *reinterpret_cast<const bf16x8*>(vr + 16 * s) : bf16x8{};
+      kf[s] = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
+      vf[s] = *reinterpret_cast<const bf16x8*>(vr + 32 * s);
     }
   }
-  // K^T of the whole tile in LDS (natural key order) for the dQ step
-  for (int u = tid; u < (BK / 4) * CPK; u += 256) {
-    const int kg = u % (BK / 4), c = u / (BK / 4);
-    uint4 r[4];
+  f32x4 dkacc[NDB], dvacc[NDB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kl = tile * BK + 4 * kg + i;
-      r[i] = kl < tkv ? *reinterpret_cast<const uint4*>(p.k + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * c)
-                      : make_uint4(0, 0, 0, 0);
+  for (int b = 0; b < NDB; ++b) { dkacc[b] = f32x4{}; dvacc[b] = f32x4{}; }
+
+  // staging: one 16-byte chunk of Q and one of dO per thread (D = 128);
+  // for D = 64 the first half of the threads takes Q and the second dO
+  constexpr int CHUNKS = BQ * CPR;                   // chunks per tensor
+  const int n_it = (qt_hi - qt_lo) * p.group;
+  auto load_step = [&](int it, uint4& qa, uint4& qb, float& sc) __attribute__((always_inline)) {
+    const int qt = qt_lo + it / p.group;
+    const int head = kvh * p.group + it % p.group;
+    const int32_t* pl = p.plan_kq + (size_t)qt * QP_WORDS;
+    const int l_row0 = pl[QP_LROW0], nrows = pl[QP_NROWS];
+    if (CHUNKS * 2 == 1024) {
+      const int row = tid / CPR, c = tid % CPR;
+      const int rr = min(row, nrows - 1);          // padded rows: a real row, never used (P = 0)
+      const size_t off = ((size_t)(l_row0 + rr) * p.hq + head) * D + 8 * c;
+      qa = *reinterpret_cast<const uint4*>(p.q + off);
+      qb = *reinterpret_cast<const uint4*>(p.d_o + off);
+    } else {
+      const int t = tid % CHUNKS;
+      const int row = t / CPR, c = t % CPR;
+      const int rr = min(row, nrows - 1);
+      const size_t off = ((size_t)(l_row0 + rr) * p.hq + head) * D + 8 * c;
+      qa = *reinterpret_cast<const uint4*>((tid < CHUNKS ? p.q : p.d_o) + off);
+      qb = qa;
     }
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 val;
-      if (e & 1) { val.x = bpack_hi(w0[e >> 1], w1[e >> 1]); val.y = bpack_hi(w2[e >> 1], w3[e >> 1]); }
-      else       { val.x = bpack_lo(w0[e >> 1], w1[e >> 1]); val.y = bpack_lo(w2[e >> 1], w3[e >> 1]); }
-      *reinterpret_cast<uint2*>(&kt_lds[(8 * c + e) * KTSTR + 4 * kg]) = val;
-    }
-  }
-
-  f32x16 dkacc[NDB], dvacc[NDB];
-#pragma unroll
-  for (int b = 0; b < NDB; ++b) { dkacc[b] = f32x16{}; dvacc[b] = f32x16{}; }
-
-  // dQ step assignment: d block and key range of this wave
-  const int dq_db = wave / WPD;
-  const int dq_k0 = (wave % WPD) * KPW;
-
-  for (int qt = qt_lo; qt < qt_hi; ++qt) {
-    const int32_t* pl = p.plan_q + (size_t)qt * QP_WORDS;
-    const int l_row0 = pl[QP_LROW0], g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
-    // mask PARTIAL tiles and the ragged last KV tile (padding keys beyond kv_hi)
-    const bool partial = qt < qt_flo || qt >= qt_fhi || (tile + 1) * BK > tkv;
-    for (int hs = 0; hs < p.group; ++hs) {
-      const int head = kvh * p.group + hs;
-      __syncthreads();                     // previous step done with the LDS buffers
-      // stage Q and dO rows (row-major and transposed) and the per-row scalars
-      {
-        const int which = tid / QUNITS;    // 0: Q, 1: dO (threads beyond 2*QUNITS idle)
-        const int u = tid % QUNITS;
-        if (which < 2) {
-          const uint16_t* src = which == 0 ? p.q : p.d_o;
-          uint16_t* rm = which == 0 ? q_lds : do_lds;
-          uint16_t* tr = which == 0 ? qt_lds : dot_lds;
-          const int rg = u % (BQ / 4), c = u / (BQ / 4);
-          uint4 r[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int qr = 4 * rg + i;
-            r[i] = qr < nrows ? *reinterpret_cast<const uint4*>(src + ((size_t)(l_row0 + qr) * p.hq + head) * D + 8 * c)
-                              : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(&rm[qr * RSTR + 8 * c]) = r[i];
-          }
-          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-          const int col = 4 * perm_pos4(rg);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            uint2 val;
-            if (e & 1) { val.x = bpack_hi(w0[e >> 1], w1[e >> 1]); val.y = bpack_hi(w2[e >> 1], w3[e >> 1]); }
-            else       { val.x = bpack_lo(w0[e >> 1], w1[e >> 1]); val.y = bpack_lo(w2[e >> 1], w3[e >> 1]); }
-            *reinterpret_cast<uint2*>(&tr[(8 * c + e) * TSTR + col]) = val;
-          }
+    sc = 0.f;
+    if (tid < 2 * BQ) {
+      const int row = tid & (BQ - 1);
+      if (row < nrows) {
+        const size_t idx = (size_t)head * p.tq + l_row0 + row;
+        if (tid < BQ) {
+          const float lv = p.lse[idx];
+          sc = lv == -INFINITY ? INFINITY : lv * kLog2e;   // empty row: P = 0
+        } else {
+          sc = p.delta[idx];
         }
-        if (tid >= 224) {
-          const int qr = tid - 224;
-          float l2 = INFINITY, dl = 0.f;
-          int dsr = 0;
-          if (qr < nrows) {
-            const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr];
-            l2 = lv == -INFINITY ? INFINITY : lv * kLog2e;   // empty row: P = 0
-            dl = p.delta[(size_t)head * p.tq + l_row0 + qr];
-            dsr = doc_start(p.cu, p.n_docs, g_row0 + qr);
-          }
-          lse_lds[qr] = l2;
-          delta_lds[qr] = dl;
-          dstart_lds[qr] = dsr;
-        }
+      } else {
+        sc = tid < BQ ? INFINITY : 0.f;                  // padded row: P = 0
       }
-      __syncthreads();
+    }
+  };
+  auto store_step = [&](int buf, const uint4& qa, const uint4& qb, float sc) __attribute__((always_inline)) {
+    if (CHUNKS * 2 == 1024) {
+      const int row = tid / CPR, c = tid % CPR;
+      *reinterpret_cast<uint4*>(&q_s[buf][row * QS + 8 * c]) = qa;
+      *reinterpret_cast<uint4*>(&do_s[buf][row * QS + 8 * c]) = qb;
+    } else {
+      const int t = tid % CHUNKS;
+      const int row = t / CPR, c = t % CPR;
+      *reinterpret_cast<uint4*>(&(tid < CHUNKS ? q_s : do_s)[buf][row * QS + 8 * c]) = qa;
+    }
+    if (tid < BQ) lse_s[buf][tid] = sc;
+    else if (tid < 2 * BQ) dlt_s[buf][tid - BQ] = sc;
+  };
 
-      // S = Q K^T (rows = queries, lanes = this wave's keys)
-      f32x16 sacc = f32x16{};
+  // transpose-read source offset of this lane inside a 32-row tile for the
+  // query rows {4g + e} (first read) and {16 + 4g + e} (second read)
+  const int tr_off = (4 * g + (i16 >> 2)) * QS + 4 * (i16 & 3);
+
+  if (n_it > 0) {
+    uint4 qa, qb;
+    float sc;
+    load_step(0, qa, qb, sc);
+    store_step(0, qa, qb, sc);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < n_it;
+    uint4 qa, qb;
+    float sc = 0.f;
+    if (more) load_step(it + 1, qa, qb, sc);        // next step's rows in flight
+
+    const int qt = qt_lo + it / p.group;
+    const int32_t* pl = p.plan_kq + (size_t)qt * QP_WORDS;
+    const int g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
+    const uint16_t* qs = q_s[buf];
+    const uint16_t* dos = do_s[buf];
+
+    // S = Q K^T and dP = dO V^T: rows q = 16 mb + 4 g + r, column = this lane's key
+    f32x4 sacc[2], dpacc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sacc[mb] = f32x4{};
+      dpacc[mb] = f32x4{};
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&q_lds[ln * RSTR + 16 * s + 8 * hh]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sacc, 0, 0, 0);
-      }
-      // P = exp2(s * scale * log2e - LSE * log2e); masked pairs and padded rows give 0
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse_lds[qr]));
-        if (partial) {
-          const int gi = g_row0 + qr;
-          const bool ok = key_ok && qr < nrows && key_g >= dstart_lds[qr] && key_g <= gi;
-          if (!ok) e = 0.f;
-        }
-        sacc[r] = e;
-      }
-      bf16x8 pb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const bf16x2 two = __builtin_convertvector(f32x2{sacc[8 * ks + i], sacc[8 * ks + i + 1]}, bf16x2);
-          pb[ks][i] = two[0];
-          pb[ks][i + 1] = two[1];
-        }
-      // dV^T += dO^T P
-#pragma unroll
-      for (int b = 0; b < NDB; ++b)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&dot_lds[(32 * b + ln) * TSTR + 16 * ks + 8 * hh]);
-          dvacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], dvacc[b], 0, 0, 0);
-        }
-      // dP = dO V^T
-      f32x16 dpacc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&do_lds[ln * RSTR + 16 * s + 8 * hh]);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[s], dpacc, 0, 0, 0);
-      }
-      // dS = P (dP - Delta)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
-        dpacc[r] = sacc[r] * (dpacc[r] - delta_lds[qr]);
-      }
-      bf16x8 dsb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const bf16x2 two = __builtin_convertvector(f32x2{dpacc[8 * ks + i], dpacc[8 * ks + i + 1]}, bf16x2);
-          dsb[ks][i] = two[0];
-          dsb[ks][i + 1] = two[1];
-        }
-      // dK^T += Q^T dS
-#pragma unroll
-      for (int b = 0; b < NDB; ++b)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&qt_lds[(32 * b + ln) * TSTR + 16 * ks + 8 * hh]);
-          dkacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[ks], dkacc[b], 0, 0, 0);
-        }
-      // stage dS [q][key] for the dQ step
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int qr = 16 * ks + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const __bf16 hv = dsb[ks][i];
-          ds_lds[qr * SSTR + 32 * wave + ln] = *reinterpret_cast<const uint16_t*>(&hv);
-        }
-      __syncthreads();
-      // dQ[q][d] += scale * dS K for this wave's d block and key range
-      f32x16 dqacc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KPW / 16; ++ks) {
-        const int k0 = dq_k0 + 16 * ks + 8 * hh;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ds_lds[ln * SSTR + k0]);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&kt_lds[(32 * dq_db + ln) * KTSTR + k0]);
-        dqacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dqacc, 0, 0, 0);
-      }
-      float* dqp = p.dq + (size_t)head * D + 32 * dq_db + ln;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (qr < nrows) atomicAdd(dqp + (size_t)(l_row0 + qr) * p.hq * D, dqacc[r] * p.scale);
+        const int off = (16 * mb + i16) * QS + 32 * s + 8 * g;
+        const bf16x8 qa_ = *reinterpret_cast<const bf16x8*>(&qs[off]);
+        const bf16x8 da_ = *reinterpret_cast<const bf16x8*>(&dos[off]);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_, kf[s], sacc[mb], 0, 0, 0);
+        dpacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da_, vf[s], dpacc[mb], 0, 0, 0);
       }
     }
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[buf][4 * g]);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[buf][16 + 4 * g]);
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][4 * g]);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][16 + 4 * g]);
+    float pv[8], dsv[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][r], p.scale_log2, -l0[r]));
+      pv[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][r], p.scale_log2, -l1[r]));
+    }
+    if (qt < qt_flo || qt >= qt_fhi || ragged) {
+      // allowed rows of this key: key_g <= g_row0 + qr < key_end, qr < nrows
+      const int lo = key_g - g_row0;
+      const int hi = key_ok ? min(key_end - g_row0, nrows) : lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int qr = 16 * (e >> 2) + 4 * g + (e & 3);
+        if (qr < lo || qr >= hi) pv[e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dsv[r] = pv[r] * (dpacc[0][r] - d0[r]);
+      dsv[4 + r] = pv[4 + r] * (dpacc[1][r] - d1[r]);
+    }
+    const bf16x8 pb = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+    const bf16x8 dsb = cvt8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (one k-step): the
+    // A operands gather rows {4g + e, 16 + 4g + e} of column 16 db + i16
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint16_t* dp_ = dos + tr_off + 16 * db;
+      const uint16_t* qp_ = qs + tr_off + 16 * db;
+      const bf16x8 doT = tr_operand(dp_, dp_ + 16 * QS);
+      const bf16x8 qT = tr_operand(qp_, qp_ + 16 * QS);
+      dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(doT, pb, dvacc[db], 0, 0, 0);
+      dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qT, dsb, dkacc[db], 0, 0, 0);
+    }
+    if (more) store_step(buf ^ 1, qa, qb, sc);
+    __syncthreads();
   }
 
-  // dK (scaled) and dV of this lane's key: rows d = 32 b + 8 g + 4 hh .. +4
+  // dK (scaled) and dV of this lane's key: d = 16 db + 4 g .. +4
   if (key_ok) {
-    float* dkp = p.dk + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
-    float* dvp = p.dv + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
+    float* dkp = p.dk + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * g;
+    float* dvp = p.dv + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      *reinterpret_cast<float4*>(dkp + 16 * db) =
+          make_float4(dkacc[db][0] * p.scale, dkacc[db][1] * p.scale, dkacc[db][2] * p.scale, dkacc[db][3] * p.scale);
+      *reinterpret_cast<float4*>(dvp + 16 * db) = make_float4(dvacc[db][0], dvacc[db][1], dvacc[db][2], dvacc[db][3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D, int RB, int HB>
+__global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
+  static_assert(RB * HB == 8, "eight waves per workgroup");
+  constexpr int BK = kDqBK;
+  constexpr int KS = D + 8;             // K / V row stride (bf16)
+  constexpr int CPK = D / 8;
+  constexpr int KPP = 512 / CPK;
+  constexpr int KPASS = BK / KPP;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][BK * KS];
+
+  if (p.err[0]) return;
+
+  const int w = xcd_remap(blockIdx.x, gridDim.x, p.xcd_cluster);
+  const int per_tile = p.hkv * p.n_hb;
+  const int rank = w / per_tile;
+  const int rem = w - rank * per_tile;
+  const int kvh = rem / p.n_hb;
+  const int hb = rem - kvh * p.n_hb;
+  const int tile = min(max(p.lpt_q[rank], 0), p.n_qtiles_dq - 1);
+  const int32_t* pl = p.plan_q + (size_t)tile * QP_WORDS;
+  const int l_row0 = pl[QP_LROW0], g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
+  const int kt_lo = pl[QP_KT_LO], kt_flo = pl[QP_KT_FLO], kt_fhi = pl[QP_KT_FHI], kt_hi = pl[QP_KT_HI];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
+  const int rb = wave / HB, hs = wave % HB;
+  const int head = kvh * p.group + hb * HB + hs;
+  const int qr = 32 * rb + ln;
+  const bool row_ok = qr < nrows;
+  const int gi = g_row0 + qr;
+  const size_t o_off = ((size_t)(l_row0 + qr) * p.hq + head) * D;
+  int a_lo = 0x40000000, a_w = 0;
+  float lse2 = INFINITY, dlt = 0.f;
+  if (row_ok) {
+    const int lo = max(doc_start(p.cu, p.n_docs, gi), p.kv_lo), hi = min(gi, p.kv_hi - 1);
+    if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
+    const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr];
+    lse2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
+    dlt = p.delta[(size_t)head * p.tq + l_row0 + qr];
+  }
+  bf16x8 qf[NKS], dof[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    qf[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh) : bf16x8{};
+    dof[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.d_o + o_off + 16 * s + 8 * hh) : bf16x8{};
+  }
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) dqacc[b] = f32x16{};
+
+  const int tkv = p.kv_hi - p.kv_lo;
+  const size_t kv_rstride = (size_t)p.hkv * D;
+  const uint16_t* kbase = p.k + (size_t)kvh * D;
+  const uint16_t* vbase = p.v + (size_t)kvh * D;
+  const int kc = tid % CPK, kk0 = tid / CPK;
+  auto load_rows = [&](const uint16_t* base, int kt, uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int pp = 0; pp < KPASS; ++pp) {
+      const int key = min(kt * BK + kk0 + KPP * pp, tkv - 1);   // padding keys: masked, any finite row
+      reg[pp] = *reinterpret_cast<const uint4*>(base + (size_t)key * kv_rstride + 8 * kc);
+    }
+  };
+  auto store_rows = [&](uint16_t* lds, const uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int pp = 0; pp < KPASS; ++pp)
+      *reinterpret_cast<uint4*>(&lds[(kk0 + KPP * pp) * KS + 8 * kc]) = reg[pp];
+  };
+  // transpose-read source offset for the K^T operand (keys in the S^T
+  // accumulator's permuted order, see the forward kernel)
+  const int i16 = lane & 15;
+  const int kt_off = (4 * hh + (i16 >> 2)) * KS + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+
+  const int n = kt_hi - kt_lo;
+  if (n > 0) {
+    uint4 kr[KPASS], vr[KPASS];
+    load_rows(kbase, kt_lo, kr);
+    load_rows(vbase, kt_lo, vr);
+    store_rows(k_s[0], kr);
+    store_rows(v_s[0], vr);
+  }
+  __syncthreads();
+  for (int u = 0; u < n; ++u) {
+    const int kt = kt_lo + u;
+    const int buf = u & 1;
+    uint4 kr[KPASS], vr[KPASS];
+    load_rows(kbase, min(kt + 1, kt_hi - 1), kr);    // the last tile again on the final step
+    load_rows(vbase, min(kt + 1, kt_hi - 1), vr);
+    const uint16_t* ks = k_s[buf];
+    const uint16_t* vs = v_s[buf];
+    const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int off = (32 * kb + ln) * KS + 16 * s + 8 * hh;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[off]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[off]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc, 0, 0, 0);
+      }
+      // P^T and dS^T for keys 32 kb + 8 (r / 4) + 4 hh + r % 4 of this tile
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse2));
+        if (partial) {
+          const unsigned rel = (unsigned)(p.kv_lo + kt * BK + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3) - a_lo);
+          if (rel > (unsigned)a_w) pr = 0.f;
+        }
+        ds[r] = pr * (dpacc[r] - dlt);
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bf16x8 dsb = cvt8(ds[8 * k2], ds[8 * k2 + 1], ds[8 * k2 + 2], ds[8 * k2 + 3], ds[8 * k2 + 4],
+                                ds[8 * k2 + 5], ds[8 * k2 + 6], ds[8 * k2 + 7]);
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const uint16_t* kp = ks + kt_off + (32 * kb + 16 * k2) * KS + 32 * b;
+          const bf16x8 kT = tr_operand(kp, kp + 8 * KS);
+          dqacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsb, dqacc[b], 0, 0, 0);
+        }
+      }
+    }
+    store_rows(k_s[buf ^ 1], kr);
+    store_rows(v_s[buf ^ 1], vr);
+    __syncthreads();
+  }
+
+  // dQ = scale * acc: lane's row, d = 32 b + 8 g + 4 hh .. +4 (added to dq for split-KV callers)
+  if (row_ok) {
+    float* dqp = p.dq + o_off + 4 * hh;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * b + 8 * g;
-        *reinterpret_cast<float4*>(dkp + d0) =
-            make_float4(dkacc[b][4 * g] * p.scale, dkacc[b][4 * g + 1] * p.scale, dkacc[b][4 * g + 2] * p.scale,
-                        dkacc[b][4 * g + 3] * p.scale);
-        *reinterpret_cast<float4*>(dvp + d0) =
-            make_float4(dvacc[b][4 * g], dvacc[b][4 * g + 1], dvacc[b][4 * g + 2], dvacc[b][4 * g + 3]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float4 val = make_float4(dqacc[b][4 * g4] * p.scale, dqacc[b][4 * g4 + 1] * p.scale,
+                                 dqacc[b][4 * g4 + 2] * p.scale, dqacc[b][4 * g4 + 3] * p.scale);
+        float4* dst = reinterpret_cast<float4*>(dqp + 32 * b + 8 * g4);
+        if (p.accumulate_dq) {
+          const float4 old = *dst;
+          val.x += old.x; val.y += old.y; val.z += old.z; val.w += old.w;
+        }
+        *dst = val;
       }
   }
 }
 
-hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const long long blocks = ((n + 3) / 4 + 255) / 256;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dst, n);
-  return hipGetLastError();
+// query heads per dQ work item: as many heads of the GQA group as divide it (<= 8)
+static int dq_heads_per_item(int group) {
+  return (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, bool delta_ready, hipStream_t stream) {
-  hipError_t e;
-  if (!accumulate_dq) {
-    e = launch_fill_zero(p.dq, (int64_t)p.tq * p.hq * d, stream);
-    if (e != hipSuccess) return e;
-  }
+int dq_rows_per_tile(int group) { return 32 * (8 / dq_heads_per_item(group)); }
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t stream) {
   const long long rh_threads = (long long)p.tq * p.hq * (d / 8);
   if (rh_threads > 0 && !delta_ready) {
     const long long blocks = (rh_threads + 255) / 256;
@@ -341,11 +435,30 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, bool delta_
       hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p.o, p.d_o, p.delta,
                          p.tq, p.hq);
   }
-  const long long nblk = (long long)p.n_kvtiles * p.hkv;
-  if (nblk > 0) {
-    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (d == 128) hipLaunchKernelGGL(bwd_kernel<128>, dim3((unsigned)nblk), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(bwd_kernel<64>, dim3((unsigned)nblk), dim3(256), 0, stream, p);
+  const long long nblk_kv = (long long)p.n_kvtiles * p.hkv;
+  if (nblk_kv > 0) {
+    if (nblk_kv > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (d == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)nblk_kv), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)nblk_kv), dim3(512), 0, stream, p);
+  }
+  const int hb = dq_heads_per_item(p.group);
+  BwdParams a = p;
+  a.n_hb = p.group / hb;
+  const long long nblk_q = (long long)p.n_qtiles_dq * p.hkv * a.n_hb;
+  if (nblk_q > 0) {
+    if (nblk_q > 0x7fffffffLL) return hipErrorInvalidValue;
+    dim3 grid((unsigned)nblk_q), block(512);
+    if (d == 128) {
+      if (hb == 8) hipLaunchKernelGGL((dq_kernel<128, 1, 8>), grid, block, 0, stream, a);
+      else if (hb == 4) hipLaunchKernelGGL((dq_kernel<128, 2, 4>), grid, block, 0, stream, a);
+      else if (hb == 2) hipLaunchKernelGGL((dq_kernel<128, 4, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((dq_kernel<128, 8, 1>), grid, block, 0, stream, a);
+    } else {
+      if (hb == 8) hipLaunchKernelGGL((dq_kernel<64, 1, 8>), grid, block, 0, stream, a);
+      else if (hb == 4) hipLaunchKernelGGL((dq_kernel<64, 2, 4>), grid, block, 0, stream, a);
+      else if (hb == 2) hipLaunchKernelGGL((dq_kernel<64, 4, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((dq_kernel<64, 8, 1>), grid, block, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -53,20 +53,24 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;          // [hq][tq] workspace
+  float* delta;           // [hq][tq] workspace
   const int32_t* cu;
-  const int32_t* plan_q;  // [n_qtiles][QP_WORDS] with bq = kBwdBQ
+  const int32_t* plan_kq; // [n_qtiles][QP_WORDS], 32-row query blocks (dK/dV kernel)
   const int32_t* kvdesc;  // [n_kvtiles][4] with bk = kBwdBK
   const int32_t* lpt_kv;  // [n_kvtiles]
+  const int32_t* plan_q;  // [n_qtiles_dq][QP_WORDS], forward-style tiles (dQ kernel)
+  const int32_t* lpt_q;   // [n_qtiles_dq]
   const int32_t* err;
-  int32_t n_docs, n_qtiles, n_kvtiles, hq, hkv, group, kv_lo, kv_hi, tq, xcd_cluster;
-  float scale;           // softmax scale
-  float scale_log2;      // softmax scale * log2(e)
+  int32_t n_docs, n_qtiles, n_kvtiles, n_qtiles_dq, hq, hkv, group, n_hb, kv_lo, kv_hi, tq, xcd_cluster;
+  int32_t accumulate_dq;
+  float scale;            // softmax scale
+  float scale_log2;       // softmax scale * log2(e)
 };
 
 constexpr int kFwdBK = 64;
 constexpr int kBwdBQ = 32;
 constexpr int kBwdBK = 128;
+constexpr int kDqBK = 64;
 
 hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv, int32_t* hist,
                            hipStream_t stream);
@@ -74,7 +78,7 @@ hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream);
 int fwd_rows_per_tile(int group);
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
-hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int d, bool accumulate_dq, bool delta_ready, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t stream);
+int dq_rows_per_tile(int group);
 
 }  // namespace docmask
