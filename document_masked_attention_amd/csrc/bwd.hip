@@ -26,6 +26,8 @@
 //   (v_mfma_f32_32x32x16_bf16; K^T through transpose reads).
 #include "kernels.h"
 
+#include <cstdlib>
+
 namespace docmask {
 
 // Delta = rowsum(dO * O) per (row, head), float32 from the bf16 inputs.
@@ -67,25 +69,29 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <int D>
+// HPI query heads of the group are processed per step: the K/V operand
+// registers are shared, the heads' MFMA chains are independent, and each
+// barrier covers HPI times the work.
+template <int D, int HPI>
 __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
   constexpr int BQ = kBwdBQ;            // 32 query rows per step
   constexpr int BK = kBwdBK;            // 128 keys per work item, 16 per wave
   constexpr int NKS = D / 32;           // k-steps over d (16x16x32)
   constexpr int NDB = D / 16;           // 16-wide d blocks of dK^T / dV^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int QS = D + 8;             // row stride of the Q / dO tiles (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[2][BQ * QS];
-  __shared__ __attribute__((aligned(16))) uint16_t do_s[2][BQ * QS];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float dlt_s[2][BQ];
+  using L = SwzTile<D, kSwzOctet>;      // Q / dO tile layout (row chunks + transpose reads)
+  constexpr int TE = L::kElems(BQ);     // elements of one 32-row tile
+  constexpr int NCH = 2 * HPI * BQ * CPR;   // 16-byte chunks staged per step (Q and dO of HPI heads)
+  constexpr int CPT = (NCH + 511) / 512;    // chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t qd_s[2][2 * HPI][TE];   // [buf][2h: Q, 2h+1: dO]
+  __shared__ __attribute__((aligned(16))) float lse_s[2][HPI][BQ];
+  __shared__ __attribute__((aligned(16))) float dlt_s[2][HPI][BQ];
 
   if (p.err[0]) return;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x, p.xcd_cluster);
-  const int rank = w / p.hkv;
-  const int kvh = w - rank * p.hkv;
-  const int tile = min(max(p.lpt_kv[rank], 0), p.n_kvtiles - 1);
+  const WorkItem wi = map_work(blockIdx.x, p.n_kvtiles, p.hkv, 1, p.xcd_cluster);
+  const int kvh = wi.kvh;
+  const int tile = min(max(p.lpt_kv[wi.rank], 0), p.n_kvtiles - 1);
   const int32_t* kd = p.kvdesc + (size_t)tile * 4;
   const int qt_lo = kd[0], qt_flo = kd[1], qt_fhi = kd[2], qt_hi = kd[3];
 
@@ -116,138 +122,147 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int b = 0; b < NDB; ++b) { dkacc[b] = f32x4{}; dvacc[b] = f32x4{}; }
 
-  // staging: one 16-byte chunk of Q and one of dO per thread (D = 128);
-  // for D = 64 the first half of the threads takes Q and the second dO
-  constexpr int CHUNKS = BQ * CPR;                   // chunks per tensor
-  const int n_it = (qt_hi - qt_lo) * p.group;
-  auto load_step = [&](int it, uint4& qa, uint4& qb, float& sc) __attribute__((always_inline)) {
-    const int qt = qt_lo + it / p.group;
-    const int head = kvh * p.group + it % p.group;
+  const int n_hsteps = p.group / HPI;
+  const int n_it = (qt_hi - qt_lo) * n_hsteps;
+  // staging of one step: chunk u (< NCH) = tensor t (2h: Q, 2h+1: dO of head
+  // h of the step), row, 16-byte column chunk; lse / Delta of the HPI heads
+  auto load_step = [&](int it, u32x4 (&reg)[CPT], float& sc) __attribute__((always_inline)) {
+    const int qt = qt_lo + it / n_hsteps;
+    const int head0 = kvh * p.group + (it % n_hsteps) * HPI;
     const int32_t* pl = p.plan_kq + (size_t)qt * QP_WORDS;
     const int l_row0 = pl[QP_LROW0], nrows = pl[QP_NROWS];
-    if (CHUNKS * 2 == 1024) {
-      const int row = tid / CPR, c = tid % CPR;
-      const int rr = min(row, nrows - 1);          // padded rows: a real row, never used (P = 0)
-      const size_t off = ((size_t)(l_row0 + rr) * p.hq + head) * D + 8 * c;
-      qa = *reinterpret_cast<const uint4*>(p.q + off);
-      qb = *reinterpret_cast<const uint4*>(p.d_o + off);
-    } else {
-      const int t = tid % CHUNKS;
-      const int row = t / CPR, c = t % CPR;
-      const int rr = min(row, nrows - 1);
-      const size_t off = ((size_t)(l_row0 + rr) * p.hq + head) * D + 8 * c;
-      qa = *reinterpret_cast<const uint4*>((tid < CHUNKS ? p.q : p.d_o) + off);
-      qb = qa;
-    }
+    static_for<CPT>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      const int u = tid + 512 * j;
+      if (NCH % 512 == 0 || u < NCH) {
+        const int t = u / (BQ * CPR), rc = u % (BQ * CPR);
+        const int row = rc / CPR, c = rc % CPR;
+        const int rr = min(row, nrows - 1);         // padded rows: a real row, never used (P = 0)
+        const size_t off = ((size_t)(l_row0 + rr) * p.hq + head0 + (t >> 1)) * D + 8 * c;
+        reg[j] = *reinterpret_cast<const u32x4*>(((t & 1) ? p.d_o : p.q) + off);
+      }
+    });
     sc = 0.f;
-    if (tid < 2 * BQ) {
-      const int row = tid & (BQ - 1);
+    if (tid < 2 * HPI * BQ) {
+      const int row = tid % BQ, h = (tid / BQ) % HPI;
+      const bool is_lse = tid < HPI * BQ;
       if (row < nrows) {
-        const size_t idx = (size_t)head * p.tq + l_row0 + row;
-        if (tid < BQ) {
+        const size_t idx = (size_t)(head0 + h) * p.tq + l_row0 + row;
+        if (is_lse) {
           const float lv = p.lse[idx];
           sc = lv == -INFINITY ? INFINITY : lv * kLog2e;   // empty row: P = 0
         } else {
           sc = p.delta[idx];
         }
       } else {
-        sc = tid < BQ ? INFINITY : 0.f;                  // padded row: P = 0
+        sc = is_lse ? INFINITY : 0.f;                    // padded row: P = 0
       }
     }
   };
-  auto store_step = [&](int buf, const uint4& qa, const uint4& qb, float sc) __attribute__((always_inline)) {
-    if (CHUNKS * 2 == 1024) {
-      const int row = tid / CPR, c = tid % CPR;
-      *reinterpret_cast<uint4*>(&q_s[buf][row * QS + 8 * c]) = qa;
-      *reinterpret_cast<uint4*>(&do_s[buf][row * QS + 8 * c]) = qb;
-    } else {
-      const int t = tid % CHUNKS;
-      const int row = t / CPR, c = t % CPR;
-      *reinterpret_cast<uint4*>(&(tid < CHUNKS ? q_s : do_s)[buf][row * QS + 8 * c]) = qa;
-    }
-    if (tid < BQ) lse_s[buf][tid] = sc;
-    else if (tid < 2 * BQ) dlt_s[buf][tid - BQ] = sc;
+  auto store_step = [&](int buf, const u32x4 (&reg)[CPT], float sc) __attribute__((always_inline)) {
+    static_for<CPT>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      const int u = tid + 512 * j;
+      if (NCH % 512 == 0 || u < NCH) {
+        const int t = u / (BQ * CPR), rc = u % (BQ * CPR);
+        const int row = rc / CPR, c = rc % CPR;
+        *reinterpret_cast<u32x4*>(&qd_s[buf][t][L::off(row, 8 * c)]) = reg[j];
+      }
+    });
+    if (tid < HPI * BQ) lse_s[buf][tid / BQ][tid % BQ] = sc;
+    else if (tid < 2 * HPI * BQ) dlt_s[buf][(tid / BQ) % HPI][tid % BQ] = sc;
   };
 
-  // transpose-read source offset of this lane inside a 32-row tile for the
-  // query rows {4g + e} (first read) and {16 + 4g + e} (second read)
-  const int tr_off = (4 * g + (i16 >> 2)) * QS + 4 * (i16 & 3);
+  // transpose-read source row/column of this lane inside a 32-row tile: query
+  // rows {4g + e} (first read) and {16 + 4g + e} (second read), columns
+  // 16 db + 4 (i16 % 4); the swizzle depends on the row modulo 16 only
+  const int tr_row = 4 * g + (i16 >> 2), tr_col = 4 * (i16 & 3);
 
   if (n_it > 0) {
-    uint4 qa, qb;
+    u32x4 reg[CPT];
     float sc;
-    load_step(0, qa, qb, sc);
-    store_step(0, qa, qb, sc);
+    load_step(0, reg, sc);
+    store_step(0, reg, sc);
   }
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
-    const bool more = it + 1 < n_it;
-    uint4 qa, qb;
-    float sc = 0.f;
-    if (more) load_step(it + 1, qa, qb, sc);        // next step's rows in flight
+    u32x4 reg[CPT];
+    float sc;
+    load_step(min(it + 1, n_it - 1), reg, sc);        // next step's rows in flight (last: a repeat)
 
-    const int qt = qt_lo + it / p.group;
+    const int qt = qt_lo + it / n_hsteps;
     const int32_t* pl = p.plan_kq + (size_t)qt * QP_WORDS;
     const int g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
-    const uint16_t* qs = q_s[buf];
-    const uint16_t* dos = do_s[buf];
+    const bool masked = qt < qt_flo || qt >= qt_fhi || ragged;
+    // allowed rows of this key: key_g <= g_row0 + qr < key_end, qr < nrows
+    const int lo = key_g - g_row0;
+    const int hi = key_ok ? min(key_end - g_row0, nrows) : lo;
 
-    // S = Q K^T and dP = dO V^T: rows q = 16 mb + 4 g + r, column = this lane's key
-    f32x4 sacc[2], dpacc[2];
+    bf16x8 pb[HPI], dsb[HPI];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sacc[mb] = f32x4{};
-      dpacc[mb] = f32x4{};
+    for (int h = 0; h < HPI; ++h) {
+      const uint16_t* qs = qd_s[buf][2 * h];
+      const uint16_t* dos = qd_s[buf][2 * h + 1];
+      // S = Q K^T and dP = dO V^T: rows q = 16 mb + 4 g + r, column = this lane's key
+      f32x4 sacc[2], dpacc[2];
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int off = (16 * mb + i16) * QS + 32 * s + 8 * g;
-        const bf16x8 qa_ = *reinterpret_cast<const bf16x8*>(&qs[off]);
-        const bf16x8 da_ = *reinterpret_cast<const bf16x8*>(&dos[off]);
-        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_, kf[s], sacc[mb], 0, 0, 0);
-        dpacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da_, vf[s], dpacc[mb], 0, 0, 0);
+      for (int mb = 0; mb < 2; ++mb) {
+        sacc[mb] = f32x4{};
+        dpacc[mb] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+          const int off = L::off(16 * mb + i16, 32 * s + 8 * g);
+          const bf16x8 qa_ = *reinterpret_cast<const bf16x8*>(&qs[off]);
+          const bf16x8 da_ = *reinterpret_cast<const bf16x8*>(&dos[off]);
+          sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_, kf[s], sacc[mb], 0, 0, 0);
+          dpacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da_, vf[s], dpacc[mb], 0, 0, 0);
+        }
       }
-    }
-    const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[buf][4 * g]);
-    const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[buf][16 + 4 * g]);
-    const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][4 * g]);
-    const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][16 + 4 * g]);
-    float pv[8], dsv[8];
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[buf][h][4 * g]);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[buf][h][16 + 4 * g]);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][h][4 * g]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][h][16 + 4 * g]);
+      float pv[8], dsv[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][r], p.scale_log2, -l0[r]));
-      pv[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][r], p.scale_log2, -l1[r]));
-    }
-    if (qt < qt_flo || qt >= qt_fhi || ragged) {
-      // allowed rows of this key: key_g <= g_row0 + qr < key_end, qr < nrows
-      const int lo = key_g - g_row0;
-      const int hi = key_ok ? min(key_end - g_row0, nrows) : lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int qr = 16 * (e >> 2) + 4 * g + (e & 3);
-        if (qr < lo || qr >= hi) pv[e] = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][r], p.scale_log2, -l0[r]));
+        pv[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][r], p.scale_log2, -l1[r]));
       }
-    }
+      if (masked) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dsv[r] = pv[r] * (dpacc[0][r] - d0[r]);
-      dsv[4 + r] = pv[4 + r] * (dpacc[1][r] - d1[r]);
+        for (int e = 0; e < 8; ++e) {
+          const int qr = 16 * (e >> 2) + 4 * g + (e & 3);
+          if (qr < lo || qr >= hi) pv[e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dsv[r] = pv[r] * (dpacc[0][r] - d0[r]);
+        dsv[4 + r] = pv[4 + r] * (dpacc[1][r] - d1[r]);
+      }
+      pb[h] = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      dsb[h] = cvt8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
     }
-    const bf16x8 pb = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-    const bf16x8 dsb = cvt8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-
-    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (one k-step): the
-    // A operands gather rows {4g + e, 16 + 4g + e} of column 16 db + i16
+    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows of each head (one
+    // k-step each): the A operands gather rows {4g + e, 16 + 4g + e} of
+    // column 16 db + i16.  The schedule keeps the transpose reads two
+    // (d block, head) groups ahead of the MFMAs that consume them.
+    sched_reads_ahead<NDB * HPI, 4, 2>();
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint16_t* dp_ = dos + tr_off + 16 * db;
-      const uint16_t* qp_ = qs + tr_off + 16 * db;
-      const bf16x8 doT = tr_operand(dp_, dp_ + 16 * QS);
-      const bf16x8 qT = tr_operand(qp_, qp_ + 16 * QS);
-      dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(doT, pb, dvacc[db], 0, 0, 0);
-      dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qT, dsb, dkacc[db], 0, 0, 0);
+      const int o0 = L::off(tr_row, 16 * db + tr_col), o1 = L::off(tr_row + 16, 16 * db + tr_col);
+#pragma unroll
+      for (int h = 0; h < HPI; ++h) {
+        const uint16_t* qs = qd_s[buf][2 * h];
+        const uint16_t* dos = qd_s[buf][2 * h + 1];
+        const bf16x8 doT = tr_operand(dos + o0, dos + o1);
+        const bf16x8 qT = tr_operand(qs + o0, qs + o1);
+        dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(doT, pb[h], dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qT, dsb[h], dkacc[db], 0, 0, 0);
+      }
     }
-    if (more) store_step(buf ^ 1, qa, qb, sc);
+    store_step(buf ^ 1, reg, sc);
     __syncthreads();
   }
 
@@ -269,24 +284,21 @@ template <int D, int RB, int HB>
 __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   static_assert(RB * HB == 8, "eight waves per workgroup");
   constexpr int BK = kDqBK;
-  constexpr int KS = D + 8;             // K / V row stride (bf16)
+  using L = SwzTile<D, kSwzQuad>;       // K tile: row chunks and transpose reads
+  constexpr int VS = D + 8;             // V tile: row chunks only (padded rows)
   constexpr int CPK = D / 8;
   constexpr int KPP = 512 / CPK;
   constexpr int KPASS = BK / KPP;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[2][L::kElems(BK)];
+  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][BK * VS];
 
   if (p.err[0]) return;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x, p.xcd_cluster);
-  const int per_tile = p.hkv * p.n_hb;
-  const int rank = w / per_tile;
-  const int rem = w - rank * per_tile;
-  const int kvh = rem / p.n_hb;
-  const int hb = rem - kvh * p.n_hb;
-  const int tile = min(max(p.lpt_q[rank], 0), p.n_qtiles_dq - 1);
+  const WorkItem wi = map_work(blockIdx.x, p.n_qtiles_dq, p.hkv, p.n_hb, p.xcd_cluster_q);
+  const int kvh = wi.kvh, hb = wi.hb;
+  const int tile = min(max(p.lpt_q[wi.rank], 0), p.n_qtiles_dq - 1);
   const int32_t* pl = p.plan_q + (size_t)tile * QP_WORDS;
   const int l_row0 = pl[QP_LROW0], g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
   const int kt_lo = pl[QP_KT_LO], kt_flo = pl[QP_KT_FLO], kt_fhi = pl[QP_KT_FHI], kt_hi = pl[QP_KT_HI];
@@ -323,36 +335,41 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
   const int kc = tid % CPK, kk0 = tid / CPK;
-  auto load_rows = [&](const uint16_t* base, int kt, uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
+  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < KPASS; ++pp) {
       const int key = min(kt * BK + kk0 + KPP * pp, tkv - 1);   // padding keys: masked, any finite row
-      reg[pp] = *reinterpret_cast<const uint4*>(base + (size_t)key * kv_rstride + 8 * kc);
+      reg[pp] = *reinterpret_cast<const u32x4*>(base + (size_t)key * kv_rstride + 8 * kc);
     }
   };
-  auto store_rows = [&](uint16_t* lds, const uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
+  auto store_k = [&](uint16_t* lds, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < KPASS; ++pp)
-      *reinterpret_cast<uint4*>(&lds[(kk0 + KPP * pp) * KS + 8 * kc]) = reg[pp];
+      *reinterpret_cast<u32x4*>(&lds[L::off(kk0 + KPP * pp, 8 * kc)]) = reg[pp];
   };
-  // transpose-read source offset for the K^T operand (keys in the S^T
+  auto store_v = [&](uint16_t* lds, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int pp = 0; pp < KPASS; ++pp)
+      *reinterpret_cast<u32x4*>(&lds[(kk0 + KPP * pp) * VS + 8 * kc]) = reg[pp];
+  };
+  // transpose-read source row/column for the K^T operand (keys in the S^T
   // accumulator's permuted order, see the forward kernel)
   const int i16 = lane & 15;
-  const int kt_off = (4 * hh + (i16 >> 2)) * KS + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  const int kt_row = 4 * hh + (i16 >> 2), kt_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
 
   const int n = kt_hi - kt_lo;
   if (n > 0) {
-    uint4 kr[KPASS], vr[KPASS];
+    u32x4 kr[KPASS], vr[KPASS];
     load_rows(kbase, kt_lo, kr);
     load_rows(vbase, kt_lo, vr);
-    store_rows(k_s[0], kr);
-    store_rows(v_s[0], vr);
+    store_k(k_s[0], kr);
+    store_v(v_s[0], vr);
   }
   __syncthreads();
   for (int u = 0; u < n; ++u) {
     const int kt = kt_lo + u;
     const int buf = u & 1;
-    uint4 kr[KPASS], vr[KPASS];
+    u32x4 kr[KPASS], vr[KPASS];
     load_rows(kbase, min(kt + 1, kt_hi - 1), kr);    // the last tile again on the final step
     load_rows(vbase, min(kt + 1, kt_hi - 1), vr);
     const uint16_t* ks = k_s[buf];
@@ -363,9 +380,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const int off = (32 * kb + ln) * KS + 16 * s + 8 * hh;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[off]);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[off]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[L::off(32 * kb + ln, 16 * s + 8 * hh)]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[(32 * kb + ln) * VS + 16 * s + 8 * hh]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc, 0, 0, 0);
       }
@@ -386,14 +402,14 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
                                 ds[8 * k2 + 5], ds[8 * k2 + 6], ds[8 * k2 + 7]);
 #pragma unroll
         for (int b = 0; b < NDB; ++b) {
-          const uint16_t* kp = ks + kt_off + (32 * kb + 16 * k2) * KS + 32 * b;
-          const bf16x8 kT = tr_operand(kp, kp + 8 * KS);
+          const int r0 = 32 * kb + 16 * k2 + kt_row;
+          const bf16x8 kT = tr_operand(ks + L::off(r0, 32 * b + kt_col), ks + L::off(r0 + 8, 32 * b + kt_col));
           dqacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsb, dqacc[b], 0, 0, 0);
         }
       }
     }
-    store_rows(k_s[buf ^ 1], kr);
-    store_rows(v_s[buf ^ 1], vr);
+    store_k(k_s[buf ^ 1], kr);
+    store_v(v_s[buf ^ 1], vr);
     __syncthreads();
   }
 
@@ -414,6 +430,15 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
         *dst = val;
       }
   }
+}
+
+// query heads per dK/dV step (overridable through DOCMASK_DKDV_HEADS for tuning)
+static int dkdv_heads_per_step(int group) {
+  int want = 2;
+  if (const char* v = std::getenv("DOCMASK_DKDV_HEADS")) want = std::atoi(v);
+  for (int h : {4, 2, 1})
+    if (h <= want && group % h == 0) return h;
+  return 1;
 }
 
 // query heads per dQ work item: as many heads of the GQA group as divide it (<= 8)
@@ -438,8 +463,17 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
   const long long nblk_kv = (long long)p.n_kvtiles * p.hkv;
   if (nblk_kv > 0) {
     if (nblk_kv > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (d == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)nblk_kv), dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)nblk_kv), dim3(512), 0, stream, p);
+    const int hpi = dkdv_heads_per_step(p.group);
+    dim3 grid((unsigned)nblk_kv), block(512);
+    if (d == 128) {
+      if (hpi == 4) hipLaunchKernelGGL((dkdv_kernel<128, 4>), grid, block, 0, stream, p);
+      else if (hpi == 2) hipLaunchKernelGGL((dkdv_kernel<128, 2>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((dkdv_kernel<128, 1>), grid, block, 0, stream, p);
+    } else {
+      if (hpi == 4) hipLaunchKernelGGL((dkdv_kernel<64, 4>), grid, block, 0, stream, p);
+      else if (hpi == 2) hipLaunchKernelGGL((dkdv_kernel<64, 2>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((dkdv_kernel<64, 1>), grid, block, 0, stream, p);
+    }
   }
   const int hb = dq_heads_per_item(p.group);
   BwdParams a = p;

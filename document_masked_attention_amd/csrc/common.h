@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace docmask {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -12,8 +15,20 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte staging register
 
 constexpr int kMaxChunks = 256;
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1, so that
+// register arrays indexed by i are resolved before any loop transformation.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 
@@ -58,17 +73,44 @@ __device__ __forceinline__ int32_t doc_end(const int32_t* __restrict__ cu, int32
 
 __host__ __device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
-// Block index remap so that consecutive logical work items of a cluster land on
-// the same XCD (the hardware hands workgroups to the 8 XCDs round-robin) while
-// clusters themselves are dealt round-robin over the XCDs in logical order.
-// A bijection on [0, n).
-__device__ __forceinline__ int xcd_remap(int b, int n, int cluster) {
-  const int per = 8 * cluster;
-  const int full = (n / per) * per;
-  if (b >= full) return b;
-  const int xcd = b & 7;
-  const int k = b >> 3;                 // k-th workgroup this XCD receives
-  return ((k / cluster) * 8 + xcd) * cluster + (k % cluster);
+// Work-item placement.  Logical items are (rank, kv_head, head_block) with
+// rank the LPT position of a tile.  Items are grouped in clusters of `cr`
+// consecutive ranks x all head blocks of ONE KV head: neighbouring tiles of a
+// document read overlapping K/V (query-major kernels) or Q/dO rows (key-major
+// kernel), so a cluster should run at the same time on the same XCD and share
+// its L2.  The hardware deals workgroups to the 8 XCDs round-robin, so
+// physical block b runs on XCD b % 8; clusters are dealt to XCDs in logical
+// order (keeping the LPT order across the chip).  A bijection on [0, n).
+struct WorkItem {
+  int rank, kvh, hb;
+};
+__device__ __forceinline__ WorkItem map_work(int b, int n_ranks, int hkv, int n_hb, int cr) {
+  const int csize = cr * n_hb;                      // items per cluster
+  const int per_rank = hkv * n_hb;
+  const int n = n_ranks * per_rank;
+  // XCD deal: the k-th block an XCD receives belongs to cluster (k / csize) * 8 + xcd
+  int w = b;
+  const int full = (n / (8 * csize)) * (8 * csize);
+  if (b < full) {
+    const int xcd = b & 7, k = b >> 3;
+    w = ((k / csize) * 8 + xcd) * csize + (k % csize);
+  }
+  WorkItem it;
+  const int full_ranks = (n_ranks / cr) * cr;
+  if (w < full_ranks * per_rank) {
+    const int ci = w / csize, within = w - ci * csize;
+    const int rank_block = ci / hkv;
+    it.kvh = ci - rank_block * hkv;
+    it.rank = rank_block * cr + within / n_hb;
+    it.hb = within % n_hb;
+  } else {
+    const int w2 = w - full_ranks * per_rank;
+    it.rank = full_ranks + w2 / per_rank;
+    const int rem = w2 % per_rank;
+    it.kvh = rem / n_hb;
+    it.hb = rem % n_hb;
+  }
+  return it;
 }
 
 __device__ __forceinline__ float wave_shfl_xor32(float x) {
@@ -96,6 +138,45 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+}
+
+// Row-major bf16 tiles in LDS that are read both as 16-byte row chunks (MFMA
+// operands along the row) and through transpose reads (operands down the
+// columns).  For D = 128 rows are unpadded and the 16 chunks of row r are
+// stored at chunk position c ^ f(r), with f a bijection of r mod 16 chosen for
+// the kernel's transpose-read footprint so that 16 consecutive rows reading
+// one chunk, and the transpose reads of 32 lanes, touch distinct banks:
+//   kSwzQuad:  f(r) = 4 (r mod 4) + (r / 4 mod 4)   (32 lanes read 4 rows x 64 B)
+//   kSwzOctet: f(r) = 2 (r mod 8) + (r / 8 mod 2)   (32 lanes read 8 rows x 32 B)
+// For D = 64 rows are padded by 16 bytes instead.
+enum { kSwzQuad = 0, kSwzOctet = 1 };
+template <int D, int MODE = kSwzQuad>
+struct SwzTile {
+  static constexpr int kRowElems = D == 128 ? 128 : D + 8;
+  static constexpr int kElems(int rows) { return rows * kRowElems; }
+  __device__ static __forceinline__ int f(int r) {
+    return MODE == kSwzQuad ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 7) << 1) | ((r >> 3) & 1));
+  }
+  // element offset of (row r, column col); col % 4 == 0 for transpose reads
+  __device__ static __forceinline__ int off(int r, int col) {
+    if (D == 128) return r * 128 + (((col >> 3) ^ f(r)) << 3) + (col & 7);
+    return r * kRowElems + col;
+  }
+};
+
+// Scheduling hint for a block of G groups, each `reads` LDS reads feeding
+// `mfmas` MFMAs: the reads of the first two groups are issued first, then
+// every group's MFMAs are followed by the reads of the group two ahead, so
+// LDS latency overlaps matrix work.  Only reorders; no effect on results.
+template <int G, int READS, int MFMAS>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * READS, 0);
+  static_for<G>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    __builtin_amdgcn_sched_group_barrier(kMfma, MFMAS, 0);
+    if (i + 2 < G) __builtin_amdgcn_sched_group_barrier(kDsRead, READS, 0);
+  });
 }
 
 // Two transpose reads assembled into one 8 x bf16 MFMA operand.

@@ -52,13 +52,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   if (p.err[0]) return;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x, p.xcd_cluster);
-  const int per_tile = p.hkv * p.n_hb;
-  const int rank = w / per_tile;
-  const int rem = w - rank * per_tile;
-  const int kvh = rem / p.n_hb;
-  const int hb = rem - kvh * p.n_hb;
-  const int tile = min(max(p.lpt[rank], 0), p.n_qtiles - 1);
+  const WorkItem wi = map_work(blockIdx.x, p.n_qtiles, p.hkv, p.n_hb, p.xcd_cluster);
+  const int kvh = wi.kvh, hb = wi.hb;
+  const int tile = min(max(p.lpt[wi.rank], 0), p.n_qtiles - 1);
   const int32_t* pl = p.plan + (size_t)tile * QP_WORDS;
   const int l_row0 = pl[QP_LROW0], g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
   const int kt_lo = pl[QP_KT_LO], kt_flo = pl[QP_KT_FLO], kt_fhi = pl[QP_KT_FHI], kt_hi = pl[QP_KT_HI];
@@ -102,17 +98,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // instead: their scores are always masked (P = 0 exactly), so any finite
   // K/V row will do.
   const int kc = tid % CPK, kk0 = tid / CPK;
-  auto load_rows = [&](const uint16_t* base, int kt, uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
+  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < KPASS; ++pp) {
       const int key = min(kt * BK + kk0 + KPP * pp, tkv - 1);
-      reg[pp] = *reinterpret_cast<const uint4*>(base + (size_t)key * kv_rstride + 8 * kc);
+      reg[pp] = *reinterpret_cast<const u32x4*>(base + (size_t)key * kv_rstride + 8 * kc);
     }
   };
-  auto store_rows = [&](uint16_t* lds, int stride, const uint4 (&reg)[KPASS]) __attribute__((always_inline)) {
+  auto store_rows = [&](uint16_t* lds, int stride, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < KPASS; ++pp)
-      *reinterpret_cast<uint4*>(&lds[(kk0 + KPP * pp) * stride + 8 * kc]) = reg[pp];
+      *reinterpret_cast<u32x4*>(&lds[(kk0 + KPP * pp) * stride + 8 * kc]) = reg[pp];
   };
   // transpose-read source address of this lane inside a V tile (see lds_read_tr16)
   const int i16 = lane & 15;
@@ -138,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int n = kt_hi - kt_lo;
   f32x16 s_cur[2], s_nxt[2];
   if (n > 0) {
-    uint4 kr0[KPASS], vr0[KPASS], kr1[KPASS];
+    u32x4 kr0[KPASS], vr0[KPASS], kr1[KPASS];
     load_rows(kbase, kt_lo, kr0);
     load_rows(vbase, kt_lo, vr0);
     load_rows(kbase, min(kt_lo + 1, kt_hi - 1), kr1);
@@ -154,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   auto step = [&](int u, auto has_next_c) __attribute__((always_inline)) {
     constexpr bool has_next = decltype(has_next_c)::value;
     const int kt = kt_lo + u;
-    uint4 kreg[KPASS], vreg[KPASS];
+    u32x4 kreg[KPASS], vreg[KPASS];
     if (has_next) {
       load_rows(kbase, min(kt + 2, kt_hi - 1), kreg);   // in flight during this tile's math
       load_rows(vbase, kt + 1, vreg);

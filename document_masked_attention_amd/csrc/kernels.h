@@ -61,7 +61,8 @@ struct BwdParams {
   const int32_t* plan_q;  // [n_qtiles_dq][QP_WORDS], forward-style tiles (dQ kernel)
   const int32_t* lpt_q;   // [n_qtiles_dq]
   const int32_t* err;
-  int32_t n_docs, n_qtiles, n_kvtiles, n_qtiles_dq, hq, hkv, group, n_hb, kv_lo, kv_hi, tq, xcd_cluster;
+  int32_t n_docs, n_qtiles, n_kvtiles, n_qtiles_dq, hq, hkv, group, n_hb, kv_lo, kv_hi, tq;
+  int32_t xcd_cluster, xcd_cluster_q;   // ranks per XCD cluster (dK/dV, dQ)
   int32_t accumulate_dq;
   float scale;            // softmax scale
   float scale_log2;       // softmax scale * log2(e)
