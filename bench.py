@@ -10,9 +10,11 @@ already resident in HBM when the timed region starts.
 forward 4*D*Hq*pairs, backward 10*D*Hq*pairs (five GEMM-shaped products per
 allowed pair, the QK^T recompute included); pairs = allowed (row, key) pairs
 per head.  The same run also times the forward alone, the backward alone, the
-backward's main kernel alone (the roofline line), the LSE merge of one CP
-rank's per-block partials (2 x CP chunks 3 and 12 of 16 x 8192, lognormal
-documents), and the CPU oracle on a bounded sample.
+LSE merge of one CP rank's per-block partials (2 x CP chunks 3 and 12 of
+16 x 8192, lognormal documents), and the CPU oracle on a bounded sample.
+During the timed steps the library's event timer brackets every kernel
+launch on its stream; the roofline line is the kernel with the largest share
+of the step: its algorithmic flop per launch divided by its mean launch time.
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
 """
@@ -34,7 +36,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-BWD_PMC_FILE = os.path.join(PROFILE_DIR, "bwd_kernel_T131072_bimodal_h64x8_d128_pmc.txt")
+WORKLOAD_TAG = "T131072_bimodal_h64x8_d128"
+# sources each kernel class is compiled from (a counter summary taken on other sources is stale)
+KERNEL_SOURCES = {"fwd_kernel": ["fwd.hip", "common.h", "kernels.h"],
+                  "dkdv_kernel": ["bwd.hip", "common.h", "kernels.h"],
+                  "dq_kernel": ["bwd.hip", "common.h", "kernels.h"]}
 
 
 def log(msg):
@@ -49,18 +55,23 @@ def kernel_source_hash(names) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(per_launch_algo_bytes):
-    """HBM bytes per launch of the backward kernel from the committed counter
-    summary, or None if absent or taken on a different kernel source."""
-    if not os.path.exists(BWD_PMC_FILE):
+def pmc_file(kernel: str) -> str:
+    return os.path.join(PROFILE_DIR, f"{kernel}_{WORKLOAD_TAG}_pmc.txt")
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from its committed counter summary, or
+    None if absent or taken on a different kernel source."""
+    path = pmc_file(kernel)
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     vals = {}
-    with open(BWD_PMC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash(["bwd.hip", "common.h", "kernels.h"]):
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(KERNEL_SOURCES[kernel]):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -68,7 +79,7 @@ def read_traffic(per_launch_algo_bytes):
         return None
 
 
-def cpu_baseline(w, min_tokens: int = 6144):
+def cpu_baseline(w, min_tokens: int = 14000):
     """The oracle, as it stands, on whole documents covering the first
     `min_tokens` tokens of the workload, one KV-head group (fwd + bwd)."""
     import oracle
@@ -150,9 +161,9 @@ def main():
     def fwd():
         api.attn_fwd(q, k, v, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale, out=o, lse=lse, workspace=ws_f)
 
-    def bwd(delta_ready=False):
+    def bwd():
         api.attn_bwd(q, k, v, o, lse, do, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale, dq=dq, dk=dk, dv=dv,
-                     accumulate_dq=delta_ready, delta_ready=delta_ready, workspace=ws_b)
+                     workspace=ws_b)
 
     def step():
         fwd()
@@ -175,19 +186,37 @@ def main():
     torch.cuda.synchronize()
     if api.check_errors(ws_f) != api.OK or api.check_errors(ws_b) != api.OK:
         raise RuntimeError("device-side input error")
+    api.timing_enable(True)          # events around every kernel launch, on the launch stream
     ms_step = timed(step, args.steps)
-    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step")
+    per_kernel = {}
+    for kc in range(api.N_KERNEL_CLASSES):
+        tot, n = api.timing_read(kc)
+        if n:
+            per_kernel[api.kernel_class_name(kc)] = {"launches": n, "total_ms": tot, "mean_ms": tot / n}
+    api.timing_enable(False)
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step; per kernel "
+        + ", ".join(f"{k} {v['mean_ms']:.3f} ms x{v['launches'] // args.steps}" for k, v in per_kernel.items()))
     ms_fwd = timed(fwd, args.steps)
     ms_bwd = timed(bwd, args.steps)
-    ms_bwd_main = timed(lambda: bwd(delta_ready=True), args.steps)   # scheduler + main backward kernel only
-    log(f"[bench] fwd {ms_fwd:.3f} ms, bwd {ms_bwd:.3f} ms, bwd main kernel {ms_bwd_main:.3f} ms")
+    log(f"[bench] fwd {ms_fwd:.3f} ms, bwd {ms_bwd:.3f} ms")
     step()                                            # leave consistent outputs behind
 
     value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
-    bwd_main_tflops = bwd_flop / (ms_bwd_main * 1e-3) / 1e12
-    algo_bytes = (2 * w.tq * w.hq * w.d * 2 + 2 * w.tkv * w.hkv * w.d * 2 + w.tq * w.hq * 4  # Q, dO, K, V, LSE
-                  + w.tq * w.hq * w.d * 4 + 2 * w.tkv * w.hkv * w.d * 4)                   # dQ, dK, dV
-    traffic = read_traffic(algo_bytes)
+    # algorithmic flop per launch of each attention kernel (allowed pairs only):
+    # forward QK^T + PV; dK/dV kernel QK^T recompute + dO V^T + P^T dO + dS^T Q;
+    # dQ kernel QK^T recompute + dO V^T + dS K
+    kernel_flop = {"fwd_kernel": 4.0 * w.d * w.hq * pairs, "dkdv_kernel": 8.0 * w.d * w.hq * pairs,
+                   "dq_kernel": 6.0 * w.d * w.hq * pairs}
+    dominant = max(kernel_flop, key=lambda k: per_kernel[k]["total_ms"])
+    dom_ms = per_kernel[dominant]["mean_ms"]
+    dom_tflops = kernel_flop[dominant] / (dom_ms * 1e-3) / 1e12
+    t_, h_, d_ = w.tq, w.hq, w.d
+    kernel_bytes = {   # compulsory HBM bytes per launch: each input read once, each output written once
+        "fwd_kernel": 2 * t_ * h_ * d_ * 2 + 2 * w.tkv * w.hkv * d_ * 2 + t_ * h_ * 4,
+        "dkdv_kernel": 2 * t_ * h_ * d_ * 2 + 2 * t_ * h_ * 4 + 2 * w.tkv * w.hkv * d_ * 2 + 2 * w.tkv * w.hkv * d_ * 4,
+        "dq_kernel": 2 * t_ * h_ * d_ * 2 + 2 * t_ * h_ * 4 + 2 * w.tkv * w.hkv * d_ * 2 + t_ * h_ * d_ * 4,
+    }
+    traffic = read_traffic(dominant)
     result = {
         "metric": "useful attention TFLOP/s fwd & fwd+bwd (% bf16 MFMA peak); merge GB/s",
         "value": round(value, 3),
@@ -204,18 +233,24 @@ def main():
         "config": {"workload": w.name, "seq_len": w.total, "documents": len(w.lengths), "seed": w.seed,
                    "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d, "pairs_per_head": pairs,
                    "value_is": "fwd+bwd useful TFLOP/s (fwd 4*D*Hq*pairs + bwd 10*D*Hq*pairs)"},
-        "roofline": {"bound": "mfma", "kernel": "bwd_kernel<128>",
-                     "achieved": round(bwd_main_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_main_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": dominant,
+                     "achieved": round(dom_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "algorithmic_bytes": int(algo_bytes),
-                     "launch_ms": round(ms_bwd_main, 4)},
+                     "algorithmic_flop": kernel_flop[dominant],
+                     "algorithmic_bytes": int(kernel_bytes[dominant]),
+                     "launch_ms": round(dom_ms, 4)},
         "components": {
             "fwd": {"ms": round(ms_fwd, 4), "tflops": round(fwd_flop / (ms_fwd * 1e-3) / 1e12, 3),
                     "frac_of_peak": round(fwd_flop / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "bwd": {"ms": round(ms_bwd, 4), "tflops": round(bwd_flop / (ms_bwd * 1e-3) / 1e12, 3),
                     "frac_of_peak": round(bwd_flop / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                     "tflops_8d_count": round(0.8 * bwd_flop / (ms_bwd * 1e-3) / 1e12, 3)},
+            "kernels": {k: {"launches_per_step": v["launches"] // args.steps, "mean_ms": round(v["mean_ms"], 4),
+                            **({"tflops": round(kernel_flop[k] / (v["mean_ms"] * 1e-3) / 1e12, 3),
+                                "frac_of_peak": round(kernel_flop[k] / (v["mean_ms"] * 1e-3) / 1e12
+                                                      / PEAK_BF16_TFLOPS, 4)} if k in kernel_flop else {})}
+                        for k, v in per_kernel.items()},
             "scheduler_counters": {"nonskip_tiles_128x64": int(counters[0]), "full": int(counters[1]),
                                    "partial": int(counters[2])},
         },

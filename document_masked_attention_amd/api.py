@@ -21,6 +21,9 @@ OP_FWD, OP_BWD = 1, 2
 ACCUMULATE_DQ = 1
 DELTA_READY = 2
 MAX_CHUNKS = 256
+(KERNEL_SCHEDULE, KERNEL_FWD, KERNEL_DELTA, KERNEL_DKDV, KERNEL_DQ, KERNEL_MERGE,
+ KERNEL_CONVERT) = range(7)
+N_KERNEL_CLASSES = 7
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -46,6 +49,9 @@ _SIGNATURES = {
     "docmask_check_errors": (ctypes.c_int, [_vp, _vp]),
     "docmask_f32_to_bf16": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
     "docmask_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "docmask_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "docmask_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "docmask_kernel_class_name": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
 
@@ -239,3 +245,20 @@ def f32_to_bf16(src: torch.Tensor, out=None) -> torch.Tensor:
     st = lib().docmask_f32_to_bf16(_ptr(src), _ptr(out), src.numel(), _stream())
     _check(st, "docmask_f32_to_bf16")
     return out
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (clearing the totals) or stop per-kernel event timing."""
+    _check(lib().docmask_timing_enable(1 if on else 0), "docmask_timing_enable")
+
+
+def timing_read(kernel_class: int) -> tuple[float, int]:
+    """(summed milliseconds, launches) of one kernel class since timing_enable(True)."""
+    ms = ctypes.c_double(0.0)
+    n = _i64(0)
+    _check(lib().docmask_timing_read(kernel_class, ctypes.byref(ms), ctypes.byref(n)), "docmask_timing_read")
+    return ms.value, int(n.value)
+
+
+def kernel_class_name(kernel_class: int) -> str:
+    return lib().docmask_kernel_class_name(kernel_class).decode()

@@ -453,6 +453,7 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
   if (rh_threads > 0 && !delta_ready) {
     const long long blocks = (rh_threads + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    KernelTimer timer(KC_DELTA, stream);
     if (d == 128)
       hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p.o, p.d_o, p.delta,
                          p.tq, p.hq);
@@ -465,6 +466,7 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
     if (nblk_kv > 0x7fffffffLL) return hipErrorInvalidValue;
     const int hpi = dkdv_heads_per_step(p.group);
     dim3 grid((unsigned)nblk_kv), block(512);
+    KernelTimer timer(KC_DKDV, stream);
     if (d == 128) {
       if (hpi == 4) hipLaunchKernelGGL((dkdv_kernel<128, 4>), grid, block, 0, stream, p);
       else if (hpi == 2) hipLaunchKernelGGL((dkdv_kernel<128, 2>), grid, block, 0, stream, p);
@@ -482,6 +484,7 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
   if (nblk_q > 0) {
     if (nblk_q > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nblk_q), block(512);
+    KernelTimer timer(KC_DQ, stream);
     if (d == 128) {
       if (hb == 8) hipLaunchKernelGGL((dq_kernel<128, 1, 8>), grid, block, 0, stream, a);
       else if (hb == 4) hipLaunchKernelGGL((dq_kernel<128, 2, 4>), grid, block, 0, stream, a);

@@ -253,6 +253,7 @@ hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream) {
   if (nblk == 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   dim3 grid((unsigned)nblk), block(256);
+  KernelTimer timer(KC_FWD, stream);
   if (d == 128) {
     if (hb == 4) hipLaunchKernelGGL((fwd_kernel<128, 1, 4>), grid, block, 0, stream, a);
     else if (hb == 2) hipLaunchKernelGGL((fwd_kernel<128, 2, 2>), grid, block, 0, stream, a);

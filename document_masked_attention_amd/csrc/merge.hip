@@ -85,6 +85,7 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream) {
   if (threads == 0) return hipSuccess;
   const long long blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  KernelTimer timer(KC_MERGE, stream);
   if (d == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -94,6 +95,7 @@ hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStr
   if (n <= 0) return hipSuccess;
   const long long blocks = ((n + 7) / 8 + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  KernelTimer timer(KC_CONVERT, stream);
   hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, n);
   return hipGetLastError();
 }

@@ -235,6 +235,7 @@ __global__ __launch_bounds__(1024) void lpt_kernel(const int32_t* __restrict__ k
 // ---------------------------------------------------------------- host side
 hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv, int32_t* hist,
                            hipStream_t stream) {
+  KernelTimer timer(KC_SCHEDULE, stream);
   hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(1024), 0, stream, p);
   if (p.n_qtiles > 0 && (p.plan_q || p.qdesc || p.key_q || p.counters))
     hipLaunchKernelGGL(qtile_kernel, dim3(ceil_div(p.n_qtiles, 256)), dim3(256), 0, stream, p);

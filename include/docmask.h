@@ -168,6 +168,32 @@ int docmask_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_t stre
 
 const char* docmask_strerror(int status);
 
+/* Kernel timing (instrumentation; defines no attention operation).
+ * While enabled, every kernel launch of the library is bracketed by two HIP
+ * events recorded on the launch stream, and their elapsed times are summed
+ * per kernel class.  No work is skipped or reordered; the only cost is the
+ * event records.  docmask_timing_enable(1) clears the totals and starts
+ * recording, docmask_timing_enable(0) stops it.  docmask_timing_read waits
+ * for every recorded pair, then returns the summed milliseconds and launch
+ * count of one class since the last enable; DOCMASK_EINVAL for an unknown
+ * class or null output, DOCMASK_EHIP if an event query failed.  The
+ * schedule class covers the whole tile-scheduler build of one call (its five
+ * small kernels).  Process-wide, thread-safe; the event pool lives until the
+ * process ends. */
+enum {
+  DOCMASK_KERNEL_SCHEDULE = 0,
+  DOCMASK_KERNEL_FWD = 1,
+  DOCMASK_KERNEL_DELTA = 2,
+  DOCMASK_KERNEL_DKDV = 3,
+  DOCMASK_KERNEL_DQ = 4,
+  DOCMASK_KERNEL_MERGE = 5,
+  DOCMASK_KERNEL_CONVERT = 6,
+  DOCMASK_N_KERNEL_CLASSES = 7
+};
+int docmask_timing_enable(int enable);
+int docmask_timing_read(int kernel_class, double* total_ms, int64_t* launches);
+const char* docmask_kernel_class_name(int kernel_class);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,3 +99,17 @@ def test_strerror(lib):
     for s in (api.OK, api.EINVAL, api.EUNSUPPORTED, api.EWORKSPACE, api.EHIP, api.EDEVICE_INPUT):
         assert api.strerror(s)
     assert "unknown" in api.strerror(123)
+
+
+def test_timing_controls(lib):
+    names = {api.kernel_class_name(i) for i in range(api.N_KERNEL_CLASSES)}
+    assert len(names) == api.N_KERNEL_CLASSES and "dkdv_kernel" in names and "fwd_kernel" in names
+    assert api.kernel_class_name(api.N_KERNEL_CLASSES) == "unknown"
+    api.timing_enable(True)
+    assert api.timing_read(api.KERNEL_DKDV) == (0.0, 0)      # nothing launched
+    api.timing_enable(False)
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    assert lib.docmask_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == api.EINVAL
+    assert lib.docmask_timing_read(api.N_KERNEL_CLASSES, ctypes.byref(ms), ctypes.byref(n)) == api.EINVAL
+    assert lib.docmask_timing_read(0, None, ctypes.byref(n)) == api.EINVAL
