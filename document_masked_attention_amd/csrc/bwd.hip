@@ -11,13 +11,14 @@
 // Two kernels, both deterministic (no atomics):
 //
 // * dkdv_kernel, key-major.  Work item = (KV tile of 128 keys, KV head);
-//   8 waves x 16 keys, each wave keeping its K and V rows (MFMA B operands)
-//   and its dK, dV accumulators in registers.  It walks every (32-row query
-//   block, query head of the group) that attends the tile -- the scheduler's
-//   per-KV-tile range -- with the Q and dO rows double-buffered in LDS:
+//   4 waves x 32 keys (one wave per SIMD), each lane keeping one key's K and
+//   V rows (MFMA B operands) and its dK, dV accumulators in registers.  It
+//   walks every (32-row query block, query head of the group) that attends
+//   the tile -- the scheduler's per-KV-tile range -- with the Q and dO rows
+//   double-buffered in LDS:
 //     S = Q K^T,  P = exp2(S c - LSE2),  dV^T += dO^T P,
 //     dP = dO V^T,  dS = P (dP - Delta),  dK^T += Q^T dS
-//   (v_mfma_f32_16x16x32_bf16; Q^T and dO^T come from the row-major tiles
+//   (v_mfma_f32_32x32x16_bf16; Q^T and dO^T come from the row-major tiles
 //   through LDS transpose reads).
 // * dq_kernel, query-major, shaped like the forward.  Work item = (query tile,
 //   KV head, block of query heads), 8 waves; each wave owns 32 rows x 1 head
@@ -69,213 +70,350 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
 }
 
 // ------------------------------------------------------------------ dK, dV
-// HPI query heads of the group are processed per step: the K/V operand
-// registers are shared, the heads' MFMA chains are independent, and each
-// barrier covers HPI times the work.
-template <int D, int HPI>
-__global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdParams p) {
-  constexpr int BQ = kBwdBQ;            // 32 query rows per step
-  constexpr int BK = kBwdBK;            // 128 keys per work item, 16 per wave
-  constexpr int NKS = D / 32;           // k-steps over d (16x16x32)
-  constexpr int NDB = D / 16;           // 16-wide d blocks of dK^T / dV^T
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  using L = SwzTile<D, kSwzOctet>;      // Q / dO tile layout (row chunks + transpose reads)
-  constexpr int TE = L::kElems(BQ);     // elements of one 32-row tile
-  constexpr int NCH = 2 * HPI * BQ * CPR;   // 16-byte chunks staged per step (Q and dO of HPI heads)
-  constexpr int CPT = (NCH + 511) / 512;    // chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t qd_s[2][2 * HPI][TE];   // [buf][2h: Q, 2h+1: dO]
-  __shared__ __attribute__((aligned(16))) float lse_s[2][HPI][BQ];
-  __shared__ __attribute__((aligned(16))) float dlt_s[2][HPI][BQ];
+// Work item = (KV tile of 128 keys, KV head); four waves of 32 keys, one
+// wave per SIMD.  Each lane keeps one key: its K and V rows are the MFMA B
+// operands of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16), whose
+// output tiles hold 16 query rows {8 j + 4 h + r} of that key per lane.  In
+// that register order P and dS are directly the B operands of dV^T += dO^T P
+// and dK^T += Q^T dS, with the 16-row k-step visited as rows
+// {4h .. 4h+3, 8+4h .. 8+4h+3} per half-wave h; the A operands dO^T and Q^T
+// come from the row-major LDS tiles through transpose reads in the same row
+// order.  The document mask enters as the initial value of the S
+// accumulator (0 or -inf per element), so P = exp2(S c - LSE2) and
+// dS = P (dP - Delta).
+//
+// The work is a sequence of units (32-row query block, query head), query
+// blocks from the last one down: the tiles of one document running at the
+// same time then read the same Q / dO rows together, which keeps them in L2.
+// Units are software-pipelined: region u runs the softmax of unit u on the
+// vector ALU while the matrix cores run dV / dK of unit u - 1 and S / dP of
+// unit u + 1.  Two units form a staging step; steps go through a ring of four
+// LDS buffers filled by direct global-to-LDS loads two steps ahead.
+// LSE and Delta read for padded query rows and dummy units: P = 0, dS = 0.
+__device__ const float kBwdPad[2] = {INFINITY, 0.f};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
+  constexpr int BQ = kBwdBQ;            // 32 query rows per unit
+  constexpr int BK = kBwdBK;            // 128 keys per work item, 32 per wave
+  constexpr int NKS = D / 16;           // k-steps of S and dP over d
+  constexpr int NMB = D / 32;           // 32-wide d blocks of dK^T / dV^T
+  constexpr int NBUF = 4;               // staging ring depth (steps)
+  using L = DenseTile<D>;               // Q / dO tile layout (row chunks + transpose reads)
+  constexpr int TE = L::kElems(BQ);
+  constexpr int RPL = 512 / D;          // tile rows per direct load (64 lanes x 16 bytes)
+  constexpr int WLT = BQ / RPL;         // direct loads per tile
+  constexpr int DPW = 4 * WLT / 4;      // direct loads per wave per step (2 units x Q, dO = 4 tiles)
+  constexpr int VM_PER_STEP = 1 + DPW;  // vector-memory instructions per wave per step
+  struct Stage {
+    uint16_t qd[4][TE];     // [2 j + 0: Q, 2 j + 1: dO] of unit j of the step
+    float lse[2][BQ];       // LSE * log2(e); +inf: P = 0
+    float dlt[2][BQ];       // Delta
+    float raw[256];         // loaded LSE / Delta words, one per thread
+  };
+  __shared__ __attribute__((aligned(16))) Stage st[NBUF];
 
   if (p.err[0]) return;
 
   const WorkItem wi = map_work(blockIdx.x, p.n_kvtiles, p.hkv, 1, p.xcd_cluster);
   const int kvh = wi.kvh;
-  const int tile = min(max(p.lpt_kv[wi.rank], 0), p.n_kvtiles - 1);
-  const int32_t* kd = p.kvdesc + (size_t)tile * 4;
-  const int qt_lo = kd[0], qt_flo = kd[1], qt_fhi = kd[2], qt_hi = kd[3];
+  const int tile = min(max(ld_const(p.lpt_kv, wi.rank), 0), p.n_kvtiles - 1);
+  const int qt_lo = ld_const(p.kvdesc, (size_t)tile * 4), qt_flo = ld_const(p.kvdesc, (size_t)tile * 4 + 1);
+  const int qt_fhi = ld_const(p.kvdesc, (size_t)tile * 4 + 2), qt_hi = ld_const(p.kvdesc, (size_t)tile * 4 + 3);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, i16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int tkv = p.kv_hi - p.kv_lo;
-  const int key_l = tile * BK + 16 * wave + i16;    // this lane's key (local KV row)
+  const int key_l = tile * BK + 32 * wave + l32;    // this lane's key (local KV row)
   const bool key_ok = key_l < tkv;
   const int key_g = p.kv_lo + key_l;
-  // rows that may attend this key: key_g <= i < end of its document
   const int key_end = key_ok ? doc_end(p.cu, p.n_docs, key_g) : key_g;
   const size_t kv_rstride = (size_t)p.hkv * D;
   const bool ragged = (tile + 1) * BK > tkv;
 
-  // K and V rows of this lane's key as MFMA B operands: d = 32 s + 8 g .. +8
+  // K and V rows of this lane's key as B operands: d = 16 s + 8 hh .. +8
   bf16x8 kf[NKS], vf[NKS];
   {
     const int kl = min(key_l, tkv - 1);               // padding keys: any finite row, masked below
-    const uint16_t* kr = p.k + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * g;
-    const uint16_t* vr = p.v + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * g;
+    const uint16_t* kr = p.k + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * hh;
+    const uint16_t* vr = p.v + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
-      vf[s] = *reinterpret_cast<const bf16x8*>(vr + 32 * s);
+      kf[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
+      vf[s] = *reinterpret_cast<const bf16x8*>(vr + 16 * s);
     }
   }
-  f32x4 dkacc[NDB], dvacc[NDB];
+  f32x16 dkacc[NMB], dvacc[NMB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) { dkacc[b] = f32x4{}; dvacc[b] = f32x4{}; }
+  for (int m = 0; m < NMB; ++m) { dkacc[m] = f32x16{}; dvacc[m] = f32x16{}; }
 
-  const int n_hsteps = p.group / HPI;
-  const int n_it = (qt_hi - qt_lo) * n_hsteps;
-  // staging of one step: chunk u (< NCH) = tensor t (2h: Q, 2h+1: dO of head
-  // h of the step), row, 16-byte column chunk; lse / Delta of the HPI heads
-  auto load_step = [&](int it, u32x4 (&reg)[CPT], float& sc) __attribute__((always_inline)) {
-    const int qt = qt_lo + it / n_hsteps;
-    const int head0 = kvh * p.group + (it % n_hsteps) * HPI;
-    const int32_t* pl = p.plan_kq + (size_t)qt * QP_WORDS;
-    const int l_row0 = pl[QP_LROW0], nrows = pl[QP_NROWS];
-    static_for<CPT>([&](auto jc) __attribute__((always_inline)) {
-      constexpr int j = decltype(jc)::value;
-      const int u = tid + 512 * j;
-      if (NCH % 512 == 0 || u < NCH) {
-        const int t = u / (BQ * CPR), rc = u % (BQ * CPR);
-        const int row = rc / CPR, c = rc % CPR;
-        const int rr = min(row, nrows - 1);         // padded rows: a real row, never used (P = 0)
-        const size_t off = ((size_t)(l_row0 + rr) * p.hq + head0 + (t >> 1)) * D + 8 * c;
-        reg[j] = *reinterpret_cast<const u32x4*>(((t & 1) ? p.d_o : p.q) + off);
-      }
+  const int n_units = (qt_hi - qt_lo) * p.group;
+  if (n_units == 0) {
+    // no query row attends this tile: zero gradients
+  }
+  const int n_steps = (n_units + 1) >> 1;             // the last step may hold one dummy unit
+  auto unit_qt = [&](int u) { return qt_hi - 1 - u / p.group; };
+  auto unit_head = [&](int u) { return kvh * p.group + u % p.group; };
+
+  // this thread's LSE / Delta source and padding word, fixed for the kernel
+  // (kept in registers: a per-lane choice of a parameter inside the loop
+  // would be a vector load whose wait covers the direct loads in flight)
+  const float* ld_src = ((tid >> 6) & 1) ? p.delta : p.lse;
+  const float* ld_pad = &kBwdPad[(tid >> 6) & 1];
+  asm volatile("" : "+v"(ld_src), "+v"(ld_pad));
+  // Plan words of unit u (clamped to the last unit), fetched once per unit
+  // when its step's loads are issued and carried in scalar registers.
+  struct UnitInfo {
+    int l_row0, g_row0, nrows, head, masked;
+  };
+  auto unit_info = [&](int u) __attribute__((always_inline)) -> UnitInfo {
+    u = min(u, n_units - 1);
+    const int qt = unit_qt(u);
+    UnitInfo ui;
+    ui.l_row0 = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_LROW0);
+    ui.g_row0 = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_GROW0);
+    ui.nrows = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_NROWS);
+    ui.head = unit_head(u);
+    // inside the tile's FULL range every (row, key) pair is allowed
+    ui.masked = (qt < qt_flo || qt >= qt_fhi || ragged || ui.nrows < BQ) ? 1 : 0;
+    return ui;
+  };
+  // Loads of step s (clamped to the last step; a unit past the end is a
+  // dummy with P = 0) into stage dst, all direct global-to-LDS loads (no
+  // register is written asynchronously): per wave first one dword per lane
+  // into raw[tid] (threads 0..127: LSE then Delta of unit (tid / 32) % 2, row
+  // tid % 32; padded rows, dummy units and threads >= 128 read the padding
+  // constants), then DPW 16-byte loads: load i covers tile t = i / (WLT / 4)
+  // (Q, dO of unit 0, Q, dO of unit 1), rows RPL (wave + 4 (i % (WLT / 4))) ..,
+  // lane -> row + lane / (D/8), chunk position lane % (D/8).
+  // The units' plan words come back in u0 / u1.
+  auto issue = [&](int s, Stage& dst, UnitInfo& u0, UnitInfo& u1) __attribute__((always_inline)) {
+    s = min(s, n_steps - 1);
+    u0 = unit_info(2 * s);
+    u1 = unit_info(2 * s + 1);
+    {
+      const int j = (tid >> 5) & 1, row = tid & 31;
+      const int nrows = j ? u1.nrows : u0.nrows, l_row0 = j ? u1.l_row0 : u0.l_row0;
+      const int head = j ? u1.head : u0.head;
+      const bool dummy = j && (2 * s + 1 >= n_units);
+      const float* src =
+          (tid >= 128 || row >= nrows || dummy) ? ld_pad : ld_src + (size_t)head * p.tq + l_row0 + row;
+      lds_dma4(src, &dst.raw[64 * wave]);
+    }
+    const int lr = lane / L::kChunks, pos = lane % L::kChunks;
+    static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int t = i / (WLT / 4);
+      const UnitInfo& ui = (t >> 1) ? u1 : u0;
+      const int r0 = (wave + 4 * (i % (WLT / 4))) * RPL;
+      const int r = r0 + lr;
+      const int rr = min(r, ui.nrows - 1);          // padded rows: a real row, never used (P = 0)
+      const size_t off = ((size_t)(ui.l_row0 + rr) * p.hq + ui.head) * D + 8 * L::chunk_at(r, pos);
+      lds_dma16(((t & 1) ? p.d_o : p.q) + off, &dst.qd[t][r0 * D]);
     });
-    sc = 0.f;
-    if (tid < 2 * HPI * BQ) {
-      const int row = tid % BQ, h = (tid / BQ) % HPI;
-      const bool is_lse = tid < HPI * BQ;
-      if (row < nrows) {
-        const size_t idx = (size_t)(head0 + h) * p.tq + l_row0 + row;
-        if (is_lse) {
-          const float lv = p.lse[idx];
-          sc = lv == -INFINITY ? INFINITY : lv * kLog2e;   // empty row: P = 0
-        } else {
-          sc = p.delta[idx];
-        }
+  };
+  // LSE2 / Delta of a staged step, from this thread's own loaded word (padded
+  // rows and dummy units read LSE = +inf, Delta = 0: P = 0; an empty row,
+  // LSE = -inf, likewise gets P = 0)
+  auto finish = [&](Stage& dst) __attribute__((always_inline)) {
+    const float v = dst.raw[tid];
+    if (tid < 64) {
+      dst.lse[tid >> 5][tid & 31] = v == -INFINITY ? INFINITY : v * kLog2e;
+    } else if (tid < 128) {
+      dst.dlt[(tid >> 5) & 1][tid & 31] = v;
+    }
+  };
+  // waits until at most `n` of this wave's vector-memory instructions are
+  // outstanding (the memory clobber keeps LDS reads of the staged data after it)
+  auto wait_vm = [&](auto n_c) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(n_c)::value) : "memory");
+  };
+
+  // transpose-read source of this lane: row 4 (lane / 32) + (lane / 4) % 4 of
+  // the k-step (second read: + 8), column 16 ((lane / 16) % 2) + 4 (lane % 4)
+  // of the 32-wide d block
+  const int tr_row = 4 * hh + ((lane >> 2) & 3), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // mask bias of a unit: 0 where (row, this key) is allowed, -inf elsewhere
+  auto unit_bias = [&](const UnitInfo& ui, f32x16& bias) __attribute__((always_inline)) {
+    if (ui.masked) {
+      // allowed rows: key_g <= g_row0 + qr < key_end, qr < nrows
+      const int lo = key_g - ui.g_row0;
+      const int hi = key_ok ? min(key_end - ui.g_row0, ui.nrows) : lo;
+      const unsigned span = (unsigned)max(hi - lo, 0);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        bias[e] = (unsigned)(8 * (e >> 2) + 4 * hh + (e & 3) - lo) < span ? 0.f : -INFINITY;
+    } else {
+      bias = f32x16{};
+    }
+  };
+  // One pipeline region, as NP slots in a fixed order (scheduling fences
+  // between slots).  Slot k issues
+  //   * MFMA k of dV / dK for unit A: d block m = k / 4, k-step t = (k / 2) % 2,
+  //     dV (k even, A operand dO^T) or dK (k odd, A operand Q^T);
+  //   * MFMA k of S / dP for unit B: k-step s = k / 2, S (k even, Q rows, from
+  //     the bias) or dP (k odd, dO rows, from zero);
+  //   * the softmax of the elements of unit C that fall to slot k;
+  // and the LDS reads of slot k + PF, so every operand has PF slots of
+  // matrix work to arrive.
+  constexpr int NP = 4 * NMB;           // == 2 * NKS: slots per region
+  constexpr int PF = 3;                 // operand prefetch distance (slots)
+  constexpr int EPS = 16 / NP;          // softmax elements per slot
+  auto region = [&](const Stage& sta, int ja, const bf16x8 (&pba)[2], const bf16x8 (&dsba)[2],
+                    const Stage& stb, int jb, const f32x16& bias, f32x16& sab, f32x16& dab,
+                    const Stage& stc, int jc, const f32x16& sac, const f32x16& dac, bf16x8 (&pbc)[2],
+                    bf16x8 (&dsbc)[2]) __attribute__((always_inline)) {
+    const uint16_t* a_q = sta.qd[2 * ja];
+    const uint16_t* a_do = sta.qd[2 * ja + 1];
+    const uint16_t* b_q = stb.qd[2 * jb];
+    const uint16_t* b_do = stb.qd[2 * jb + 1];
+    bf16x8 opa[NP], opb[NP];
+    auto load = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int m = k / 4, t = (k / 2) % 2, sb = k / 2;
+      const int o0 = L::off(16 * t + tr_row, 32 * m + tr_col);
+      const int o1 = L::off(16 * t + 8 + tr_row, 32 * m + tr_col);
+      const uint16_t* ta = (k % 2) ? a_q : a_do;
+      opa[k] = tr_operand(ta + o0, ta + o1);
+      const uint16_t* tb = (k % 2) ? b_do : b_q;
+      opb[k] = *reinterpret_cast<const bf16x8*>(&tb[L::off(l32, 16 * sb + 8 * hh)]);
+    };
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      l4[jj] = *reinterpret_cast<const f32x4*>(&stc.lse[jc][8 * jj + 4 * hh]);
+      d4[jj] = *reinterpret_cast<const f32x4*>(&stc.dlt[jc][8 * jj + 4 * hh]);
+    }
+    static_for<PF>([&](auto kc) __attribute__((always_inline)) { load(kc); });
+    float pv[16], dsv[16];
+    static_for<NP>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int m = k / 4, t = (k / 2) % 2, sb = k / 2;
+      if constexpr (k + PF < NP) load(std::integral_constant<int, k + PF>{});
+      if constexpr (k % 2 == 0) {
+        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], pba[t], dvacc[m], 0, 0, 0);
+        sab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], kf[sb], sb == 0 ? bias : sab, 0, 0, 0);
       } else {
-        sc = is_lse ? INFINITY : 0.f;                    // padded row: P = 0
+        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], dsba[t], dkacc[m], 0, 0, 0);
+        dab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], vf[sb], sb == 0 ? f32x16{} : dab, 0, 0, 0);
       }
-    }
-  };
-  auto store_step = [&](int buf, const u32x4 (&reg)[CPT], float sc) __attribute__((always_inline)) {
-    static_for<CPT>([&](auto jc) __attribute__((always_inline)) {
-      constexpr int j = decltype(jc)::value;
-      const int u = tid + 512 * j;
-      if (NCH % 512 == 0 || u < NCH) {
-        const int t = u / (BQ * CPR), rc = u % (BQ * CPR);
-        const int row = rc / CPR, c = rc % CPR;
-        *reinterpret_cast<u32x4*>(&qd_s[buf][t][L::off(row, 8 * c)]) = reg[j];
-      }
+      static_for<EPS>([&](auto ec) __attribute__((always_inline)) {
+        constexpr int e = k * EPS + decltype(ec)::value;
+        const float pe =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sac[e], p.scale_log2, -l4[e / 4][e % 4]));
+        pv[e] = pe;
+        dsv[e] = pe * (dac[e] - d4[e / 4][e % 4]);
+      });
+      __builtin_amdgcn_sched_barrier(0);
     });
-    if (tid < HPI * BQ) lse_s[buf][tid / BQ][tid % BQ] = sc;
-    else if (tid < 2 * HPI * BQ) dlt_s[buf][(tid / BQ) % HPI][tid % BQ] = sc;
-  };
-
-  // transpose-read source row/column of this lane inside a 32-row tile: query
-  // rows {4g + e} (first read) and {16 + 4g + e} (second read), columns
-  // 16 db + 4 (i16 % 4); the swizzle depends on the row modulo 16 only
-  const int tr_row = 4 * g + (i16 >> 2), tr_col = 4 * (i16 & 3);
-
-  if (n_it > 0) {
-    u32x4 reg[CPT];
-    float sc;
-    load_step(0, reg, sc);
-    store_step(0, reg, sc);
-  }
-  __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    u32x4 reg[CPT];
-    float sc;
-    load_step(min(it + 1, n_it - 1), reg, sc);        // next step's rows in flight (last: a repeat)
-
-    const int qt = qt_lo + it / n_hsteps;
-    const int32_t* pl = p.plan_kq + (size_t)qt * QP_WORDS;
-    const int g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
-    const bool masked = qt < qt_flo || qt >= qt_fhi || ragged;
-    // allowed rows of this key: key_g <= g_row0 + qr < key_end, qr < nrows
-    const int lo = key_g - g_row0;
-    const int hi = key_ok ? min(key_end - g_row0, nrows) : lo;
-
-    bf16x8 pb[HPI], dsb[HPI];
 #pragma unroll
-    for (int h = 0; h < HPI; ++h) {
-      const uint16_t* qs = qd_s[buf][2 * h];
-      const uint16_t* dos = qd_s[buf][2 * h + 1];
-      // S = Q K^T and dP = dO V^T: rows q = 16 mb + 4 g + r, column = this lane's key
-      f32x4 sacc[2], dpacc[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        sacc[mb] = f32x4{};
-        dpacc[mb] = f32x4{};
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-          const int off = L::off(16 * mb + i16, 32 * s + 8 * g);
-          const bf16x8 qa_ = *reinterpret_cast<const bf16x8*>(&qs[off]);
-          const bf16x8 da_ = *reinterpret_cast<const bf16x8*>(&dos[off]);
-          sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_, kf[s], sacc[mb], 0, 0, 0);
-          dpacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da_, vf[s], dpacc[mb], 0, 0, 0);
-        }
-      }
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[buf][h][4 * g]);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[buf][h][16 + 4 * g]);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][h][4 * g]);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dlt_s[buf][h][16 + 4 * g]);
-      float pv[8], dsv[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][r], p.scale_log2, -l0[r]));
-        pv[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][r], p.scale_log2, -l1[r]));
-      }
-      if (masked) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int qr = 16 * (e >> 2) + 4 * g + (e & 3);
-          if (qr < lo || qr >= hi) pv[e] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        dsv[r] = pv[r] * (dpacc[0][r] - d0[r]);
-        dsv[4 + r] = pv[4 + r] * (dpacc[1][r] - d1[r]);
-      }
-      pb[h] = cvt8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      dsb[h] = cvt8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    for (int t = 0; t < 2; ++t) {
+      pbc[t] = cvt8(pv[8 * t], pv[8 * t + 1], pv[8 * t + 2], pv[8 * t + 3], pv[8 * t + 4], pv[8 * t + 5],
+                    pv[8 * t + 6], pv[8 * t + 7]);
+      dsbc[t] = cvt8(dsv[8 * t], dsv[8 * t + 1], dsv[8 * t + 2], dsv[8 * t + 3], dsv[8 * t + 4], dsv[8 * t + 5],
+                     dsv[8 * t + 6], dsv[8 * t + 7]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows of each head (one
-    // k-step each): the A operands gather rows {4g + e, 16 + 4g + e} of
-    // column 16 db + i16.  The schedule keeps the transpose reads two
-    // (d block, head) groups ahead of the MFMAs that consume them.
-    sched_reads_ahead<NDB * HPI, 4, 2>();
+    asm volatile("" : "+v"(pbc[0]), "+v"(pbc[1]), "+v"(dsbc[0]), "+v"(dsbc[1]));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // S (from the bias) and dP of unit j of stage cur, alone (pipeline start)
+  auto sdp = [&](const Stage& cur, int j, const f32x16& bias, f32x16& sa, f32x16& da) __attribute__((always_inline)) {
+    const uint16_t* qs = cur.qd[2 * j];
+    const uint16_t* dos = cur.qd[2 * j + 1];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int o0 = L::off(tr_row, 16 * db + tr_col), o1 = L::off(tr_row + 16, 16 * db + tr_col);
+    for (int s = 0; s < NKS; ++s) {
+      const int off = L::off(l32, 16 * s + 8 * hh);
+      const bf16x8 qa_ = *reinterpret_cast<const bf16x8*>(&qs[off]);
+      const bf16x8 da_ = *reinterpret_cast<const bf16x8*>(&dos[off]);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kf[s], s == 0 ? bias : sa, 0, 0, 0);
+      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da_, vf[s], s == 0 ? f32x16{} : da, 0, 0, 0);
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS for unit j of stage cur, alone (pipeline end)
+  auto dvdk = [&](const Stage& cur, int j, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2])
+      __attribute__((always_inline)) {
+    const uint16_t* qs = cur.qd[2 * j];
+    const uint16_t* dos = cur.qd[2 * j + 1];
 #pragma unroll
-      for (int h = 0; h < HPI; ++h) {
-        const uint16_t* qs = qd_s[buf][2 * h];
-        const uint16_t* dos = qd_s[buf][2 * h + 1];
+    for (int m = 0; m < NMB; ++m) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int o0 = L::off(16 * t + tr_row, 32 * m + tr_col);
+        const int o1 = L::off(16 * t + 8 + tr_row, 32 * m + tr_col);
         const bf16x8 doT = tr_operand(dos + o0, dos + o1);
         const bf16x8 qT = tr_operand(qs + o0, qs + o1);
-        dvacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(doT, pb[h], dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qT, dsb[h], dkacc[db], 0, 0, 0);
+        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doT, pb[t], dvacc[m], 0, 0, 0);
+        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsb[t], dkacc[m], 0, 0, 0);
       }
     }
-    store_step(buf ^ 1, reg, sc);
+  };
+
+  if (n_units > 0) {
+    // prologue: steps 0 and 1 staged; S / dP of unit 0
+    UnitInfo ic0, ic1, in0, in1;      // plan words of steps s and s + 1
+    issue(0, st[0], ic0, ic1);
+    issue(1, st[1], in0, in1);
+    wait_vm(std::integral_constant<int, 0>{});
+    finish(st[0]);
+    finish(st[1]);
+    // the key's document end and the K / V operands are in registers before
+    // any later loads are in flight
+    asm volatile("" ::"v"(key_end));
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
     __syncthreads();
+
+    f32x16 sa[2], da[2], bias;
+    bf16x8 pb[2][2], dsb[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) { pb[1][t] = bf16x8{}; dsb[1][t] = bf16x8{}; }   // unit -1: adds zero
+    unit_bias(ic0, bias);
+    sdp(st[0], 0, bias, sa[0], da[0]);
+    for (int s = 0; s < n_steps; ++s) {
+      Stage& cur = st[s & (NBUF - 1)];
+      Stage& prv = st[(s + NBUF - 1) & (NBUF - 1)];      // unit 2s - 1 (s = 0: zero operands on stage 0)
+      Stage& nx1 = st[(s + 1) & (NBUF - 1)];
+      Stage& nx2 = st[(s + 2) & (NBUF - 1)];
+      // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
+      UnitInfo i20, i21;
+      issue(s + 2, nx2, i20, i21);
+      unit_bias(ic1, bias);
+      __builtin_amdgcn_sched_barrier(0);
+      region(s == 0 ? cur : prv, 1, pb[1], dsb[1], cur, 1, bias, sa[1], da[1], cur, 0, sa[0], da[0], pb[0], dsb[0]);
+      // ---- step s + 1 staged (its loads were issued two regions ago)
+      if (s > 0) {
+        wait_vm(std::integral_constant<int, VM_PER_STEP>{});
+        finish(nx1);
+      }
+      __syncthreads();
+      unit_bias(in0, bias);
+      // ---- region 2s + 1: dV, dK (2s) | S, dP (2s + 2) | softmax(2s + 1)
+      __builtin_amdgcn_sched_barrier(0);
+      region(cur, 0, pb[0], dsb[0], nx1, 0, bias, sa[0], da[0], cur, 1, sa[1], da[1], pb[1], dsb[1]);
+      ic0 = in0; ic1 = in1; in0 = i20; in1 = i21;
+    }
+    // the last unit's dV, dK (a dummy unit adds zero)
+    dvdk(st[(n_steps - 1) & (NBUF - 1)], 1, pb[1], dsb[1]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads
   }
 
-  // dK (scaled) and dV of this lane's key: d = 16 db + 4 g .. +4
+  // dK (scaled) and dV of this lane's key: d = 32 m + 8 j + 4 hh .. +4
   if (key_ok) {
-    float* dkp = p.dk + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * g;
-    float* dvp = p.dv + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * g;
+    float* dkp = p.dk + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
+    float* dvp = p.dv + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      *reinterpret_cast<float4*>(dkp + 16 * db) =
-          make_float4(dkacc[db][0] * p.scale, dkacc[db][1] * p.scale, dkacc[db][2] * p.scale, dkacc[db][3] * p.scale);
-      *reinterpret_cast<float4*>(dvp + 16 * db) = make_float4(dvacc[db][0], dvacc[db][1], dvacc[db][2], dvacc[db][3]);
-    }
+    for (int m = 0; m < NMB; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 32 * m + 8 * j;
+        *reinterpret_cast<float4*>(dkp + c) =
+            make_float4(dkacc[m][4 * j] * p.scale, dkacc[m][4 * j + 1] * p.scale, dkacc[m][4 * j + 2] * p.scale,
+                        dkacc[m][4 * j + 3] * p.scale);
+        *reinterpret_cast<float4*>(dvp + c) =
+            make_float4(dvacc[m][4 * j], dvacc[m][4 * j + 1], dvacc[m][4 * j + 2], dvacc[m][4 * j + 3]);
+      }
   }
 }
 
@@ -284,7 +422,7 @@ template <int D, int RB, int HB>
 __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   static_assert(RB * HB == 8, "eight waves per workgroup");
   constexpr int BK = kDqBK;
-  using L = SwzTile<D, kSwzQuad>;       // K tile: row chunks and transpose reads
+  using L = SwzTile<D>;                 // K tile: row chunks and transpose reads
   constexpr int VS = D + 8;             // V tile: row chunks only (padded rows)
   constexpr int CPK = D / 8;
   constexpr int KPP = 512 / CPK;
@@ -432,15 +570,6 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   }
 }
 
-// query heads per dK/dV step (overridable through DOCMASK_DKDV_HEADS for tuning)
-static int dkdv_heads_per_step(int group) {
-  int want = 2;
-  if (const char* v = std::getenv("DOCMASK_DKDV_HEADS")) want = std::atoi(v);
-  for (int h : {4, 2, 1})
-    if (h <= want && group % h == 0) return h;
-  return 1;
-}
-
 // query heads per dQ work item: as many heads of the GQA group as divide it (<= 8)
 static int dq_heads_per_item(int group) {
   return (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
@@ -464,18 +593,10 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
   const long long nblk_kv = (long long)p.n_kvtiles * p.hkv;
   if (nblk_kv > 0) {
     if (nblk_kv > 0x7fffffffLL) return hipErrorInvalidValue;
-    const int hpi = dkdv_heads_per_step(p.group);
-    dim3 grid((unsigned)nblk_kv), block(512);
+    dim3 grid((unsigned)nblk_kv), block(256);
     KernelTimer timer(KC_DKDV, stream);
-    if (d == 128) {
-      if (hpi == 4) hipLaunchKernelGGL((dkdv_kernel<128, 4>), grid, block, 0, stream, p);
-      else if (hpi == 2) hipLaunchKernelGGL((dkdv_kernel<128, 2>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((dkdv_kernel<128, 1>), grid, block, 0, stream, p);
-    } else {
-      if (hpi == 4) hipLaunchKernelGGL((dkdv_kernel<64, 4>), grid, block, 0, stream, p);
-      else if (hpi == 2) hipLaunchKernelGGL((dkdv_kernel<64, 2>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((dkdv_kernel<64, 1>), grid, block, 0, stream, p);
-    }
+    if (d == 128) hipLaunchKernelGGL((dkdv_kernel<128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((dkdv_kernel<64>), grid, block, 0, stream, p);
   }
   const int hb = dq_heads_per_item(p.group);
   BwdParams a = p;

@@ -143,26 +143,70 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
 // Row-major bf16 tiles in LDS that are read both as 16-byte row chunks (MFMA
 // operands along the row) and through transpose reads (operands down the
 // columns).  For D = 128 rows are unpadded and the 16 chunks of row r are
-// stored at chunk position c ^ f(r), with f a bijection of r mod 16 chosen for
-// the kernel's transpose-read footprint so that 16 consecutive rows reading
-// one chunk, and the transpose reads of 32 lanes, touch distinct banks:
-//   kSwzQuad:  f(r) = 4 (r mod 4) + (r / 4 mod 4)   (32 lanes read 4 rows x 64 B)
-//   kSwzOctet: f(r) = 2 (r mod 8) + (r / 8 mod 2)   (32 lanes read 8 rows x 32 B)
+// stored at chunk position c ^ f(r), with f a bijection of r mod 16, so that
+// 16 consecutive rows reading one chunk, and 32 lanes reading 4 rows x 64 B
+// through transpose reads, touch distinct banks:
+//   f(r) = 4 (r mod 4) + (r / 4 mod 4).
 // For D = 64 rows are padded by 16 bytes instead.
-enum { kSwzQuad = 0, kSwzOctet = 1 };
-template <int D, int MODE = kSwzQuad>
+template <int D>
 struct SwzTile {
   static constexpr int kRowElems = D == 128 ? 128 : D + 8;
   static constexpr int kElems(int rows) { return rows * kRowElems; }
-  __device__ static __forceinline__ int f(int r) {
-    return MODE == kSwzQuad ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 7) << 1) | ((r >> 3) & 1));
-  }
+  __device__ static __forceinline__ int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
   // element offset of (row r, column col); col % 4 == 0 for transpose reads
   __device__ static __forceinline__ int off(int r, int col) {
     if (D == 128) return r * 128 + (((col >> 3) ^ f(r)) << 3) + (col & 7);
     return r * kRowElems + col;
   }
 };
+
+// The same two read patterns on unpadded rows for both head sizes, so that a
+// tile is a dense run of 16-byte chunks that direct global-to-LDS loads can
+// fill (64 lanes write 1 KB contiguously).  Chunk c of row r sits at c ^ f(r):
+//   D = 128 (16 chunks, a row spans all 64 banks): f(r) = 4 (r mod 4) + (r / 4 mod 4)
+//   D = 64 (8 chunks, two rows share the banks): f(r) = 4 (r / 2 mod 2) + (r / 4 mod 4)
+// For D = 64 the 16 rows of a chunk read split into two parities of 8 rows
+// with distinct f, and rows 4a + e, 4a + e + 2 of a transpose read use
+// opposite halves of the row's banks.
+template <int D>
+struct DenseTile {
+  static_assert(D == 64 || D == 128, "head size");
+  static constexpr int kChunks = D / 8;
+  static constexpr int kElems(int rows) { return rows * D; }
+  __device__ static __forceinline__ int f(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+  __device__ static __forceinline__ int off(int r, int col) { return r * D + (((col >> 3) ^ f(r)) << 3) + (col & 7); }
+  // logical chunk stored at chunk position pos of row r
+  __device__ static __forceinline__ int chunk_at(int r, int pos) { return pos ^ f(r); }
+};
+
+// Direct 16-byte global-to-LDS load: lane l's 16 bytes land at lds_base +
+// 16 l (lds_base wave-uniform).  Completion is counted by vmcnt.  Issued as
+// inline assembly, so the compiler neither tracks the LDS write (the caller
+// waits with wait_vmem() and a barrier before any wave reads the buffer) nor
+// inserts conservative waits before unrelated LDS reads.
+__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
+  const uint32_t lds_addr =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Load of a word the kernel never writes (scheduler tables), through the
+// constant address space so that a wave-uniform index becomes a scalar load.
+__device__ __forceinline__ int32_t ld_const(const int32_t* base, size_t idx) {
+  return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
+}
+
+// Direct 4-byte global-to-LDS load: lane l's dword lands at lds_base + 4 l.
+__device__ __forceinline__ void lds_dma4(const void* gptr, void* lds_base) {
+  const uint32_t lds_addr =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Wait until this wave's global loads (including direct-to-LDS ones) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
 
 // Scheduling hint for a block of G groups, each `reads` LDS reads feeding
 // `mfmas` MFMAs: the reads of the first two groups are issued first, then
