@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+                    help="also run the f32->bf16 conversion over 1 GiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of it",
@@ -261,12 +261,15 @@ def main():
     if not args.no_merge:
         result["components"]["merge"] = bench_merge(api, torch, dev, upload, args.steps)
     if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
+        # a streaming kernel of known size for scaling HBM byte counters: the
+        # library's f32 -> bf16 conversion reads 1 GiB and writes 512 MiB
+        a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty(1 << 28, dtype=torch.bfloat16, device=dev)
         for _ in range(3):
-            b.copy_(a)
+            api.f32_to_bf16(a, out=b)
         torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = {"read": a.numel() * 4, "write": a.numel() * 4}
+        result["copy_calibration_bytes"] = {"kernel": "f32_to_bf16_kernel", "read": a.numel() * 4,
+                                            "write": b.numel() * 2}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)
