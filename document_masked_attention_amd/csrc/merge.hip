@@ -9,9 +9,33 @@
 
 namespace docmask {
 
+// Weighted sum of the 16-byte slices of partials [q0, q0 + QB) with LSE values
+// lq (-inf: empty partial, weight 0, not read); all slices are requested
+// before any is used.
+template <int QB>
+__device__ __forceinline__ void merge_group(const u32x4* op, size_t o_stride, int q0, const float (&lq)[QB],
+                                            float lse2, float (&acc)[8]) {
+  float wgt[QB];
+  u32x4 raw[QB];
+#pragma unroll
+  for (int i = 0; i < QB; ++i) {
+    wgt[i] = lq[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i], kLog2e, -lse2));
+    raw[i] = u32x4{0u, 0u, 0u, 0u};
+    if (lq[i] != -INFINITY) raw[i] = __builtin_nontemporal_load(op + (size_t)(q0 + i) * o_stride);
+  }
+#pragma unroll
+  for (int i = 0; i < QB; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] += wgt[i] * __uint_as_float(raw[i][k] << 16);
+      acc[2 * k + 1] += wgt[i] * __uint_as_float(raw[i][k] & 0xffff0000u);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   constexpr int CPR = D / 8;                        // threads per (row, head)
+  constexpr int QB = 8;                             // partials per batch of loads
   const size_t n_rh = (size_t)p.rows * p.hq;
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t rh = gid / CPR;
@@ -20,39 +44,54 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int row = (int)(rh / p.hq), head = (int)(rh % p.hq);
   const size_t lse_stride = n_rh;                   // elements between partials
   const float* lp = p.lse_parts + (size_t)head * p.rows + row;
-  float m = -INFINITY;
-  for (int q = 0; q < p.n_parts; ++q) m = fmaxf(m, lp[q * lse_stride]);
+  const int np = p.n_parts;
+  const u32x4* op = reinterpret_cast<const u32x4*>(p.o_parts + rh * D + 8 * c);
+  const size_t o_stride = n_rh * D / 8;             // 16-byte slices between partials
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float out_lse = -INFINITY;
-  if (m != -INFINITY) {
-    const float m2 = m * kLog2e;
-    float s = 0.f;
-    for (int q = 0; q < p.n_parts; ++q) s += __builtin_amdgcn_exp2f(__builtin_fmaf(lp[q * lse_stride], kLog2e, -m2));
-    const float lse2 = m2 + __log2f(s);             // log2 of the merged sum
-    out_lse = lse2 * kLn2;
-    const uint16_t* op = p.o_parts + rh * D + 8 * c;
-    const size_t o_stride = n_rh * D;
-    for (int q = 0; q < p.n_parts; ++q) {
-      const float lq = lp[q * lse_stride];
-      if (lq == -INFINITY) continue;                // empty partial: weight 0, not read
-      const float wgt = __builtin_amdgcn_exp2f(__builtin_fmaf(lq, kLog2e, -lse2));
-      const uint4 raw = *reinterpret_cast<const uint4*>(op + q * o_stride);
-      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+  if (np <= QB) {
+    // all LSE values in registers: one round of LSE loads, one of slices
+    float lq[QB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wgt * __uint_as_float(wds[i] << 16);
-        acc[2 * i + 1] += wgt * __uint_as_float(wds[i] & 0xffff0000u);
+    for (int i = 0; i < QB; ++i) lq[i] = i < np ? lp[i * lse_stride] : -INFINITY;
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < QB; ++i) m = fmaxf(m, lq[i]);
+    if (m != -INFINITY) {
+      const float m2 = m * kLog2e;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < QB; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i], kLog2e, -m2));
+      const float lse2 = m2 + __log2f(s);           // log2 of the merged sum
+      out_lse = lse2 * kLn2;
+      merge_group<QB>(op, o_stride, 0, lq, lse2, acc);
+    }
+  } else {
+    float m = -INFINITY;
+#pragma unroll 4
+    for (int q = 0; q < np; ++q) m = fmaxf(m, lp[q * lse_stride]);
+    if (m != -INFINITY) {
+      const float m2 = m * kLog2e;
+      float s = 0.f;
+#pragma unroll 4
+      for (int q = 0; q < np; ++q) s += __builtin_amdgcn_exp2f(__builtin_fmaf(lp[q * lse_stride], kLog2e, -m2));
+      const float lse2 = m2 + __log2f(s);
+      out_lse = lse2 * kLn2;
+      for (int q0 = 0; q0 < np; q0 += QB) {
+        float lq[QB];
+#pragma unroll
+        for (int i = 0; i < QB; ++i) lq[i] = q0 + i < np ? lp[(q0 + i) * lse_stride] : -INFINITY;
+        merge_group<QB>(op, o_stride, q0, lq, lse2, acc);
       }
     }
   }
-  uint4 outv;
-  uint32_t* ow = reinterpret_cast<uint32_t*>(&outv);
+  u32x4 outv;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bf16x2 two = __builtin_convertvector(f32x2{acc[2 * i], acc[2 * i + 1]}, bf16x2);
-    ow[i] = *reinterpret_cast<const uint32_t*>(&two);
+    outv[i] = __builtin_bit_cast(uint32_t, two);
   }
-  *reinterpret_cast<uint4*>(p.o_out + rh * D + 8 * c) = outv;
+  __builtin_nontemporal_store(outv, reinterpret_cast<u32x4*>(p.o_out + rh * D + 8 * c));
   if (c == 0) p.lse_out[(size_t)head * p.rows + row] = out_lse;
 }
 
