@@ -232,6 +232,68 @@ __global__ __launch_bounds__(1024) void lpt_kernel(const int32_t* __restrict__ k
   }
 }
 
+// The same ordering with the histogram in LDS (dynamic shared memory of
+// max_key + 1 ints), for key ranges up to kLptLdsKeys: LDS atomics instead of
+// contended global ones.
+constexpr int kLptLdsKeys = 8192;
+__global__ __launch_bounds__(1024) void lpt_lds_kernel(const int32_t* __restrict__ keys, int32_t n,
+                                                       int32_t max_key, int32_t* __restrict__ order) {
+  extern __shared__ int32_t lhist[];
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  const int nk = max_key + 1;
+  for (int k = tid; k < nk; k += 1024) lhist[k] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&lhist[min(max(keys[i], 0), max_key)], 1);
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  // exclusive scan over keys in descending order: start[k] = #tiles with key > k
+  for (int base = 0; base < nk; base += 1024) {
+    const int idx = base + tid;
+    const int key = max_key - idx;
+    const int h = idx < nk ? lhist[key] : 0;
+    scan[tid] = h;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int x = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += x;
+      __syncthreads();
+    }
+    const int incl = scan[tid];
+    const int c = carry;
+    __syncthreads();
+    if (idx < nk) lhist[key] = c + incl - h;
+    if (tid == 1023) carry = c + incl;
+    __syncthreads();
+  }
+  // stable placement: each wave takes 64 consecutive tiles in turn (chunk
+  // order across waves is kept by a ticket so that ties stay in index order)
+  if (tid < 64) {
+    int bits = 0;
+    while (bits < 31 && (1 << bits) <= max_key) ++bits;
+    const unsigned long long lt = (1ull << tid) - 1ull;
+    for (int base = 0; base < n; base += 64) {
+      const int i = base + tid;
+      const bool valid = i < n;
+      const int key = valid ? min(max(keys[i], 0), max_key) : 0;
+      unsigned long long m = __ballot(valid);
+      for (int b = 0; b < bits; ++b) {
+        const int bit = (key >> b) & 1;
+        const unsigned long long ones = __ballot(valid && bit);
+        m &= bit ? ones : ~ones;
+      }
+      const int rank = __popcll(m & lt);
+      const int leader = valid ? __ffsll((long long)m) - 1 : 0;
+      int pos0 = 0;
+      if (valid && tid == leader) pos0 = atomicAdd(&lhist[key], __popcll(m));
+      pos0 = __shfl(pos0, leader, 64);
+      if (valid && pos0 + rank < n) order[pos0 + rank] = i;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host side
 hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv, int32_t* hist,
                            hipStream_t stream) {
@@ -243,12 +305,16 @@ hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv
     hipLaunchKernelGGL(kvtile_kernel, dim3(ceil_div(p.n_kvtiles, 256)), dim3(256), 0, stream, p);
   if (p.need && p.ch.n > 0)
     hipLaunchKernelGGL(need_kernel, dim3(ceil_div(p.ch.n, 256)), dim3(256), 0, stream, p);
-  if (lpt_q && p.n_qtiles > 0)
-    hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(1024), 0, stream, (const int32_t*)p.key_q, p.n_qtiles,
-                       p.n_kvtiles, hist, lpt_q);
-  if (lpt_kv && p.n_kvtiles > 0)
-    hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(1024), 0, stream, (const int32_t*)p.key_kv, p.n_kvtiles,
-                       p.n_qtiles, hist, lpt_kv);
+  // keys of Q tiles are KV-tile counts (<= n_kvtiles) and vice versa
+  auto lpt = [&](const int32_t* keys, int32_t n, int32_t max_key, int32_t* order) {
+    if (max_key + 1 <= kLptLdsKeys)
+      hipLaunchKernelGGL(lpt_lds_kernel, dim3(1), dim3(1024), (size_t)(max_key + 1) * sizeof(int32_t), stream, keys,
+                         n, max_key, order);
+    else
+      hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(1024), 0, stream, keys, n, max_key, hist, order);
+  };
+  if (lpt_q && p.n_qtiles > 0) lpt((const int32_t*)p.key_q, p.n_qtiles, p.n_kvtiles, lpt_q);
+  if (lpt_kv && p.n_kvtiles > 0) lpt((const int32_t*)p.key_kv, p.n_kvtiles, p.n_qtiles, lpt_kv);
   return hipGetLastError();
 }
 
