@@ -473,12 +473,17 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
   const int kc = tid % CPK, kk0 = tid / CPK;
-  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
+  // tile base (wave-uniform) + a 32-bit byte offset per lane; padding keys
+  // clamp to the last real row (masked, any finite row will do)
+  const uint32_t row_bytes = (uint32_t)(kv_rstride * sizeof(uint16_t));
+  uint32_t loff[KPASS];
 #pragma unroll
-    for (int pp = 0; pp < KPASS; ++pp) {
-      const int key = min(kt * BK + kk0 + KPP * pp, tkv - 1);   // padding keys: masked, any finite row
-      reg[pp] = *reinterpret_cast<const u32x4*>(base + (size_t)key * kv_rstride + 8 * kc);
-    }
+  for (int pp = 0; pp < KPASS; ++pp) loff[pp] = (uint32_t)(kk0 + KPP * pp) * row_bytes + 16u * kc;
+  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
+    const char* tb = reinterpret_cast<const char*>(base + (size_t)kt * BK * kv_rstride);
+    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes + 16u * kc;
+#pragma unroll
+    for (int pp = 0; pp < KPASS; ++pp) reg[pp] = *reinterpret_cast<const u32x4*>(tb + min(loff[pp], lim));
   };
   auto store_k = [&](uint16_t* lds, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
@@ -523,15 +528,19 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc, 0, 0, 0);
       }
+      // document mask (PARTIAL and ragged tiles only, a wave-uniform branch):
+      // masked scores become -inf, so P = 0
+      if (partial) {
+        const int rel0 = p.kv_lo + kt * BK + 32 * kb + 4 * hh - a_lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((unsigned)(rel0 + 8 * (r >> 2) + (r & 3)) > (unsigned)a_w) sacc[r] = -INFINITY;
+      }
       // P^T and dS^T for keys 32 kb + 8 (r / 4) + 4 hh + r % 4 of this tile
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse2));
-        if (partial) {
-          const unsigned rel = (unsigned)(p.kv_lo + kt * BK + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3) - a_lo);
-          if (rel > (unsigned)a_w) pr = 0.f;
-        }
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse2));
         ds[r] = pr * (dpacc[r] - dlt);
       }
 #pragma unroll

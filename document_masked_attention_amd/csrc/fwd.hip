@@ -98,12 +98,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // instead: their scores are always masked (P = 0 exactly), so any finite
   // K/V row will do.
   const int kc = tid % CPK, kk0 = tid / CPK;
-  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
+  const uint32_t row_bytes = (uint32_t)(kv_rstride * sizeof(uint16_t));
+  // tile base (wave-uniform) + a 32-bit byte offset per lane; rows past the
+  // end of the KV range clamp to the last real row (same column chunk, so
+  // clamping the byte offset clamps the row)
+  uint32_t loff[KPASS];
 #pragma unroll
-    for (int pp = 0; pp < KPASS; ++pp) {
-      const int key = min(kt * BK + kk0 + KPP * pp, tkv - 1);
-      reg[pp] = *reinterpret_cast<const u32x4*>(base + (size_t)key * kv_rstride + 8 * kc);
-    }
+  for (int pp = 0; pp < KPASS; ++pp) loff[pp] = (uint32_t)(kk0 + KPP * pp) * row_bytes + 16u * kc;
+  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
+    const char* tb = reinterpret_cast<const char*>(base + (size_t)kt * BK * kv_rstride);
+    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes + 16u * kc;
+#pragma unroll
+    for (int pp = 0; pp < KPASS; ++pp) reg[pp] = *reinterpret_cast<const u32x4*>(tb + min(loff[pp], lim));
   };
   auto store_rows = [&](uint16_t* lds, int stride, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
 #pragma unroll
