@@ -78,9 +78,9 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
 // and dK^T += Q^T dS, with the 16-row k-step visited as rows
 // {4h .. 4h+3, 8+4h .. 8+4h+3} per half-wave h; the A operands dO^T and Q^T
 // come from the row-major LDS tiles through transpose reads in the same row
-// order.  The document mask enters as the initial value of the S
-// accumulator (0 or -inf per element), so P = exp2(S c - LSE2) and
-// dS = P (dP - Delta).
+// order.  dP starts from -Delta, so dS = P dP; P = exp2(S c - LSE2), with
+// the scores of disallowed pairs set to -inf (only units outside the tile's
+// FULL range, in a branch between pipeline regions).
 //
 // The work is a sequence of units (32-row query block, query head), query
 // blocks from the last one down: the tiles of one document running at the
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   struct Stage {
     uint16_t qd[4][TE];     // [2 j + 0: Q, 2 j + 1: dO] of unit j of the step
     float lse[2][BQ];       // LSE * log2(e); +inf: P = 0
-    float dlt[2][BQ];       // Delta
+    float ndl[2][BQ];       // -Delta
     float raw[256];         // loaded LSE / Delta words, one per thread
   };
   __shared__ __attribute__((aligned(16))) Stage st[NBUF];
@@ -213,15 +213,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       lds_dma16(((t & 1) ? p.d_o : p.q) + off, &dst.qd[t][r0 * D]);
     });
   };
-  // LSE2 / Delta of a staged step, from this thread's own loaded word (padded
-  // rows and dummy units read LSE = +inf, Delta = 0: P = 0; an empty row,
-  // LSE = -inf, likewise gets P = 0)
+  // LSE2 / -Delta of a staged step, from this thread's own loaded word
+  // (padded rows and dummy units read LSE = +inf, Delta = 0: P = 0; an empty
+  // row, LSE = -inf, likewise gets P = 0)
   auto finish = [&](Stage& dst) __attribute__((always_inline)) {
     const float v = dst.raw[tid];
     if (tid < 64) {
       dst.lse[tid >> 5][tid & 31] = v == -INFINITY ? INFINITY : v * kLog2e;
     } else if (tid < 128) {
-      dst.dlt[(tid >> 5) & 1][tid & 31] = v;
+      dst.ndl[(tid >> 5) & 1][tid & 31] = -v;
     }
   };
   // waits until at most `n` of this wave's vector-memory instructions are
@@ -235,26 +235,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // of the 32-wide d block
   const int tr_row = 4 * hh + ((lane >> 2) & 3), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // mask bias of a unit: 0 where (row, this key) is allowed, -inf elsewhere
-  auto unit_bias = [&](const UnitInfo& ui, f32x16& bias) __attribute__((always_inline)) {
-    if (ui.masked) {
-      // allowed rows: key_g <= g_row0 + qr < key_end, qr < nrows
-      const int lo = key_g - ui.g_row0;
-      const int hi = key_ok ? min(key_end - ui.g_row0, ui.nrows) : lo;
-      const unsigned span = (unsigned)max(hi - lo, 0);
+  // document mask of a unit on its S accumulators: scores of (row, this key)
+  // pairs that are not allowed become -inf (P = 0).  Only units outside the
+  // tile's FULL range need it; the caller branches on ui.masked.
+  auto unit_mask = [&](const UnitInfo& ui, f32x16& sa) __attribute__((always_inline)) {
+    // allowed rows: key_g <= g_row0 + qr < key_end, qr < nrows
+    const int lo = key_g - ui.g_row0;
+    const int hi = key_ok ? min(key_end - ui.g_row0, ui.nrows) : lo;
+    const unsigned span = (unsigned)max(hi - lo, 0);
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        bias[e] = (unsigned)(8 * (e >> 2) + 4 * hh + (e & 3) - lo) < span ? 0.f : -INFINITY;
-    } else {
-      bias = f32x16{};
-    }
+    for (int e = 0; e < 16; ++e)
+      if ((unsigned)(8 * (e >> 2) + 4 * hh + (e & 3) - lo) >= span) sa[e] = -INFINITY;
   };
   // One pipeline region, as NP slots in a fixed order (scheduling fences
   // between slots).  Slot k issues
   //   * MFMA k of dV / dK for unit A: d block m = k / 4, k-step t = (k / 2) % 2,
   //     dV (k even, A operand dO^T) or dK (k odd, A operand Q^T);
   //   * MFMA k of S / dP for unit B: k-step s = k / 2, S (k even, Q rows, from
-  //     the bias) or dP (k odd, dO rows, from zero);
+  //     zero) or dP (k odd, dO rows, from -Delta);
   //   * the softmax of the elements of unit C that fall to slot k;
   // and the LDS reads of slot k + PF, so every operand has PF slots of
   // matrix work to arrive.
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   constexpr int PF = 3;                 // operand prefetch distance (slots)
   constexpr int EPS = 16 / NP;          // softmax elements per slot
   auto region = [&](const Stage& sta, int ja, const bf16x8 (&pba)[2], const bf16x8 (&dsba)[2],
-                    const Stage& stb, int jb, const f32x16& bias, f32x16& sab, f32x16& dab,
+                    const Stage& stb, int jb, f32x16& sab, f32x16& dab,
                     const Stage& stc, int jc, const f32x16& sac, const f32x16& dac, bf16x8 (&pbc)[2],
                     bf16x8 (&dsbc)[2]) __attribute__((always_inline)) {
     const uint16_t* a_q = sta.qd[2 * ja];
@@ -280,11 +278,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       const uint16_t* tb = (k % 2) ? b_do : b_q;
       opb[k] = *reinterpret_cast<const bf16x8*>(&tb[L::off(l32, 16 * sb + 8 * hh)]);
     };
-    f32x4 l4[4], d4[4];
+    f32x4 l4[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) l4[jj] = *reinterpret_cast<const f32x4*>(&stc.lse[jc][8 * jj + 4 * hh]);
+    f32x16 ndb;                                   // -Delta of unit B's rows: dP starts from it
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      l4[jj] = *reinterpret_cast<const f32x4*>(&stc.lse[jc][8 * jj + 4 * hh]);
-      d4[jj] = *reinterpret_cast<const f32x4*>(&stc.dlt[jc][8 * jj + 4 * hh]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&stb.ndl[jb][8 * jj + 4 * hh]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ndb[4 * jj + r] = d4[r];
     }
     static_for<PF>([&](auto kc) __attribute__((always_inline)) { load(kc); });
     float pv[16], dsv[16];
@@ -294,17 +296,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       if constexpr (k + PF < NP) load(std::integral_constant<int, k + PF>{});
       if constexpr (k % 2 == 0) {
         dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], pba[t], dvacc[m], 0, 0, 0);
-        sab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], kf[sb], sb == 0 ? bias : sab, 0, 0, 0);
+        sab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], kf[sb], sb == 0 ? f32x16{} : sab, 0, 0, 0);
       } else {
         dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], dsba[t], dkacc[m], 0, 0, 0);
-        dab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], vf[sb], sb == 0 ? f32x16{} : dab, 0, 0, 0);
+        dab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], vf[sb], sb == 0 ? ndb : dab, 0, 0, 0);
       }
       static_for<EPS>([&](auto ec) __attribute__((always_inline)) {
         constexpr int e = k * EPS + decltype(ec)::value;
         const float pe =
             __builtin_amdgcn_exp2f(__builtin_fmaf(sac[e], p.scale_log2, -l4[e / 4][e % 4]));
         pv[e] = pe;
-        dsv[e] = pe * (dac[e] - d4[e / 4][e % 4]);
+        dsv[e] = pe * dac[e];
       });
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -318,17 +320,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     asm volatile("" : "+v"(pbc[0]), "+v"(pbc[1]), "+v"(dsbc[0]), "+v"(dsbc[1]));
     __builtin_amdgcn_sched_barrier(0);
   };
-  // S (from the bias) and dP of unit j of stage cur, alone (pipeline start)
-  auto sdp = [&](const Stage& cur, int j, const f32x16& bias, f32x16& sa, f32x16& da) __attribute__((always_inline)) {
+  // S and dP (from -Delta) of unit j of stage cur, alone (pipeline start)
+  auto sdp = [&](const Stage& cur, int j, f32x16& sa, f32x16& da) __attribute__((always_inline)) {
     const uint16_t* qs = cur.qd[2 * j];
     const uint16_t* dos = cur.qd[2 * j + 1];
+    f32x16 nd;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cur.ndl[j][8 * jj + 4 * hh]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nd[4 * jj + r] = d4[r];
+    }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const int off = L::off(l32, 16 * s + 8 * hh);
       const bf16x8 qa_ = *reinterpret_cast<const bf16x8*>(&qs[off]);
       const bf16x8 da_ = *reinterpret_cast<const bf16x8*>(&dos[off]);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kf[s], s == 0 ? bias : sa, 0, 0, 0);
-      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da_, vf[s], s == 0 ? f32x16{} : da, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kf[s], s == 0 ? f32x16{} : sa, 0, 0, 0);
+      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da_, vf[s], s == 0 ? nd : da, 0, 0, 0);
     }
   };
   // dV^T += dO^T P and dK^T += Q^T dS for unit j of stage cur, alone (pipeline end)
@@ -365,12 +374,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     for (int s = 0; s < NKS; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
     __syncthreads();
 
-    f32x16 sa[2], da[2], bias;
+    f32x16 sa[2], da[2];
     bf16x8 pb[2][2], dsb[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) { pb[1][t] = bf16x8{}; dsb[1][t] = bf16x8{}; }   // unit -1: adds zero
-    unit_bias(ic0, bias);
-    sdp(st[0], 0, bias, sa[0], da[0]);
+    sdp(st[0], 0, sa[0], da[0]);
+    if (ic0.masked) unit_mask(ic0, sa[0]);
     for (int s = 0; s < n_steps; ++s) {
       Stage& cur = st[s & (NBUF - 1)];
       Stage& prv = st[(s + NBUF - 1) & (NBUF - 1)];      // unit 2s - 1 (s = 0: zero operands on stage 0)
@@ -379,19 +388,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
       UnitInfo i20, i21;
       issue(s + 2, nx2, i20, i21);
-      unit_bias(ic1, bias);
       __builtin_amdgcn_sched_barrier(0);
-      region(s == 0 ? cur : prv, 1, pb[1], dsb[1], cur, 1, bias, sa[1], da[1], cur, 0, sa[0], da[0], pb[0], dsb[0]);
+      region(s == 0 ? cur : prv, 1, pb[1], dsb[1], cur, 1, sa[1], da[1], cur, 0, sa[0], da[0], pb[0], dsb[0]);
+      if (ic1.masked) unit_mask(ic1, sa[1]);
       // ---- step s + 1 staged (its loads were issued two regions ago)
       if (s > 0) {
         wait_vm(std::integral_constant<int, VM_PER_STEP>{});
         finish(nx1);
       }
       __syncthreads();
-      unit_bias(in0, bias);
       // ---- region 2s + 1: dV, dK (2s) | S, dP (2s + 2) | softmax(2s + 1)
       __builtin_amdgcn_sched_barrier(0);
-      region(cur, 0, pb[0], dsb[0], nx1, 0, bias, sa[0], da[0], cur, 1, sa[1], da[1], pb[1], dsb[1]);
+      region(cur, 0, pb[0], dsb[0], nx1, 0, sa[0], da[0], cur, 1, sa[1], da[1], pb[1], dsb[1]);
+      if (in0.masked) unit_mask(in0, sa[0]);
       ic0 = in0; ic1 = in1; in0 = i20; in1 = i21;
     }
     // the last unit's dV, dK (a dummy unit adds zero)
