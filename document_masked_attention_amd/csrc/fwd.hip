@@ -22,8 +22,10 @@
 // The accumulator row order of S^T is {0-3, 8-11 | 4-7, 12-15} per 16 keys for
 // the two lane halves; the V^T operand is gathered in that same key order from
 // the row-major V tile with LDS transpose reads (ds_read_b64_tr_b16).
-// K/V tiles are double-buffered in LDS with one barrier per tile; the MFMAs of
-// the next tile's S^T are issued before the current tile's softmax.
+// K/V tiles are double-buffered in LDS (filled by direct global-to-LDS loads)
+// with one barrier per tile; after a tile's softmax the MFMAs of the next
+// tile's S^T and of this tile's PV run back to back, while the other wave on
+// the SIMD works on its softmax.
 #include "kernels.h"
 
 #include <type_traits>
@@ -43,8 +45,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int KSTR = D + 8;           // K row stride (bf16): 16-byte row reads hit distinct banks
   constexpr int VSTR = D + 32;          // V row stride: transpose reads of 4 rows hit distinct banks
   constexpr int CPK = D / 8;            // 16-byte chunks per key row
-  constexpr int KPP = 256 / CPK;        // keys per load pass
-  constexpr int KPASS = BK / KPP;
+  constexpr int KCH = KSTR / 8, VCH = VSTR / 8;       // 16-byte slots per LDS row (data + padding)
+  constexpr int WLK = BK * KCH / 64, WLV = BK * VCH / 64;   // direct loads (64 slots) per tile
+  static_assert(BK * KCH % 64 == 0 && BK * VCH % 64 == 0, "tiles are whole direct loads");
+  constexpr int DPK = (WLK + 3) / 4, DPV = (WLV + 3) / 4;   // per wave (the last may be idle)
   constexpr int NKS = D / 16;           // k-steps of QK^T
   constexpr int NDB = D / 32;           // 32-wide d blocks of O
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KSTR];
@@ -93,28 +97,43 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
 
-  // global -> register -> LDS staging of K and V tiles (row-major, 16-byte
-  // chunks).  Padding keys of a ragged last tile load the last real row
-  // instead: their scores are always masked (P = 0 exactly), so any finite
-  // K/V row will do.
-  const int kc = tid % CPK, kk0 = tid / CPK;
+  // K and V tiles reach LDS by direct global-to-LDS loads (no staging
+  // registers; completion by this wave's vmcnt, then a barrier).  A tile of
+  // padded rows is a run of 16-byte slots; direct load j (of a wave: j = wave
+  // + 4 i) fills slots 64 j .. 64 j + 63, and lane l's slot 64 j + l is row
+  // q / CH, chunk q % CH (q = 64 j + l).  Padding slots load any real chunk
+  // of the row (never read).  The tile base is wave-uniform; each lane adds a
+  // 32-bit byte offset.  Padding keys of a ragged last tile read the last real
+  // row instead: their scores are always masked (P = 0 exactly), so any
+  // finite K/V row will do.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)(kv_rstride * sizeof(uint16_t));
-  // tile base (wave-uniform) + a 32-bit byte offset per lane; rows past the
-  // end of the KV range clamp to the last real row (same column chunk, so
-  // clamping the byte offset clamps the row)
-  uint32_t loff[KPASS];
+  uint32_t krow[DPK], kchk[DPK], vrow[DPV], vchk[DPV];
 #pragma unroll
-  for (int pp = 0; pp < KPASS; ++pp) loff[pp] = (uint32_t)(kk0 + KPP * pp) * row_bytes + 16u * kc;
-  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
-    const char* tb = reinterpret_cast<const char*>(base + (size_t)kt * BK * kv_rstride);
-    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes + 16u * kc;
+  for (int i = 0; i < DPK; ++i) {
+    const int q = (wave_u + 4 * i) * 64 + lane;
+    krow[i] = (uint32_t)(q / KCH) * row_bytes;
+    kchk[i] = 16u * (uint32_t)min(q % KCH, CPK - 1);
+  }
 #pragma unroll
-    for (int pp = 0; pp < KPASS; ++pp) reg[pp] = *reinterpret_cast<const u32x4*>(tb + min(loff[pp], lim));
+  for (int i = 0; i < DPV; ++i) {
+    const int q = (wave_u + 4 * i) * 64 + lane;
+    vrow[i] = (uint32_t)(q / VCH) * row_bytes;
+    vchk[i] = 16u * (uint32_t)min(q % VCH, CPK - 1);
+  }
+  auto issue_k = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
+    const char* tb = reinterpret_cast<const char*>(kbase + (size_t)kt * BK * kv_rstride);
+    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < DPK; ++i)
+      if (wave_u + 4 * i < WLK) lds_dma16(tb + min(krow[i], lim) + kchk[i], lds + (wave_u + 4 * i) * 512);
   };
-  auto store_rows = [&](uint16_t* lds, int stride, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
+  auto issue_v = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
+    const char* tb = reinterpret_cast<const char*>(vbase + (size_t)kt * BK * kv_rstride);
+    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes;
 #pragma unroll
-    for (int pp = 0; pp < KPASS; ++pp)
-      *reinterpret_cast<u32x4*>(&lds[(kk0 + KPP * pp) * stride + 8 * kc]) = reg[pp];
+    for (int i = 0; i < DPV; ++i)
+      if (wave_u + 4 * i < WLV) lds_dma16(tb + min(vrow[i], lim) + vchk[i], lds + (wave_u + 4 * i) * 512);
   };
   // transpose-read source address of this lane inside a V tile (see lds_read_tr16)
   const int i16 = lane & 15;
@@ -133,34 +152,35 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     }
   };
 
-  // Software pipeline over the n tiles (index u = kt - kt_lo): K tile u lives in
-  // k_lds[u & 1] and V tile u in v_lds[u & 1].  Iteration u issues the MFMAs of
-  // S(u + 1) before the softmax of tile u so the matrix cores run while the
-  // VALU works; K is therefore staged two tiles ahead and V one tile ahead.
+  // Pipeline over the n tiles (index u = kt - kt_lo): K tile u lives in
+  // k_lds[u & 1] and V tile u in v_lds[u & 1].  Step u computes S(u + 1) right
+  // after the softmax of tile u, so K is staged two tiles ahead and V one.
   const int n = kt_hi - kt_lo;
-  f32x16 s_cur[2], s_nxt[2];
+  f32x16 s_cur[2];
   if (n > 0) {
-    u32x4 kr0[KPASS], vr0[KPASS], kr1[KPASS];
-    load_rows(kbase, kt_lo, kr0);
-    load_rows(vbase, kt_lo, vr0);
-    load_rows(kbase, min(kt_lo + 1, kt_hi - 1), kr1);
-    store_rows(k_lds[0], KSTR, kr0);
-    store_rows(v_lds[0], VSTR, vr0);
-    store_rows(k_lds[1], KSTR, kr1);
+    issue_k(kt_lo, k_lds[0]);
+    issue_v(kt_lo, v_lds[0]);
+    issue_k(min(kt_lo + 1, kt_hi - 1), k_lds[1]);
+    wait_vmem();
     __syncthreads();
     compute_s(k_lds[0], s_cur);
     __syncthreads();                  // every wave has read K tile 0 before it is overwritten
   }
+  // the Q operands are in registers before any tile loads are in flight (a
+  // first use inside the loop would wait for all of them)
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) asm volatile("" ::"v"(qf[s]));
   // One pipeline step; `has_next` is a compile-time flag so that the steady-state
   // body has no branches between the next tile's MFMAs and this tile's softmax.
   auto step = [&](int u, auto has_next_c) __attribute__((always_inline)) {
     constexpr bool has_next = decltype(has_next_c)::value;
     const int kt = kt_lo + u;
-    u32x4 kreg[KPASS], vreg[KPASS];
     if (has_next) {
-      load_rows(kbase, min(kt + 2, kt_hi - 1), kreg);   // in flight during this tile's math
-      load_rows(vbase, kt + 1, vreg);
-      compute_s(k_lds[(u + 1) & 1], s_nxt);
+      // K tile u + 2 (the last tile again near the end) into the buffer K tile u
+      // left, V tile u + 1 into the one V tile u - 1 left; in flight during this
+      // tile's math
+      issue_k(min(kt + 2, kt_hi - 1), k_lds[u & 1]);
+      issue_v(kt + 1, v_lds[(u + 1) & 1]);
     }
 
     // document mask on PARTIAL tiles and on the ragged last tile (its padding
@@ -206,6 +226,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         pf[2 * kb + (r >> 3)][(r & 7) + 1] = two[1];
       }
     l_run += rs;
+    // S of the next tile, into the registers this tile's softmax has just
+    // read; those MFMAs and this tile's PV run back to back
+    if (has_next) compute_s(k_lds[(u + 1) & 1], s_cur);
 
     // O^T += V^T P^T, 16 keys per step; V^T comes from the row-major V tile
     // through transpose reads, in the accumulator's permuted key order
@@ -219,11 +242,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[b], 0, 0, 0);
       }
     if (has_next) {
-      store_rows(k_lds[u & 1], KSTR, kreg);         // K tile u + 2 (the last tile again near the end)
-      store_rows(v_lds[(u + 1) & 1], VSTR, vreg);
+      wait_vmem();
       __syncthreads();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     }
   };
   for (int u = 0; u + 1 < n; ++u) step(u, std::true_type{});
