@@ -8,57 +8,30 @@
 //   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 // with dK and dV summed over the query heads of each KV group.
 //
-// Two kernels, both deterministic (no atomics):
+// Two kernels, both deterministic (no atomics), launched in this order:
 //
+// * dq_kernel, query-major, shaped like the forward.  Work item = (query tile,
+//   KV head, block of query heads), 8 waves; each wave owns 32 rows x 1 head.
+//   It first forms Delta of its rows (unless the caller supplied it) from the
+//   dO operands it holds and the O rows, and stores it; then it walks the
+//   tile's KV range:
+//     S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T
+//   (v_mfma_f32_32x32x16_bf16; K^T through transpose reads).
 // * dkdv_kernel, key-major.  Work item = (KV tile of 128 keys, KV head);
 //   4 waves x 32 keys (one wave per SIMD), each lane keeping one key's K and
 //   V rows (MFMA B operands) and its dK, dV accumulators in registers.  It
 //   walks every (32-row query block, query head of the group) that attends
 //   the tile -- the scheduler's per-KV-tile range -- with the Q and dO rows
-//   double-buffered in LDS:
+//   staged in LDS:
 //     S = Q K^T,  P = exp2(S c - LSE2),  dV^T += dO^T P,
 //     dP = dO V^T,  dS = P (dP - Delta),  dK^T += Q^T dS
 //   (v_mfma_f32_32x32x16_bf16; Q^T and dO^T come from the row-major tiles
 //   through LDS transpose reads).
-// * dq_kernel, query-major, shaped like the forward.  Work item = (query tile,
-//   KV head, block of query heads), 8 waves; each wave owns 32 rows x 1 head
-//   and walks the tile's KV range:
-//     S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T
-//   (v_mfma_f32_32x32x16_bf16; K^T through transpose reads).
 #include "kernels.h"
 
 #include <cstdlib>
 
 namespace docmask {
-
-// Delta = rowsum(dO * O) per (row, head), float32 from the bf16 inputs.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
-                                                        const uint16_t* __restrict__ d_o,
-                                                        float* __restrict__ delta, int32_t tq, int32_t hq) {
-  constexpr int CPR = D / 8;
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t rh = gid / CPR;
-  const int c = (int)(gid % CPR);
-  const size_t n_rh = (size_t)tq * hq;
-  float acc = 0.f;
-  if (rh < n_rh) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + rh * D + 8 * c);
-    const uint4 b = *reinterpret_cast<const uint4*>(d_o + rh * D + 8 * c);
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc += __uint_as_float(aw[i] << 16) * __uint_as_float(bw[i] << 16);
-      acc += __uint_as_float(aw[i] & 0xffff0000u) * __uint_as_float(bw[i] & 0xffff0000u);
-    }
-  }
-#pragma unroll
-  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (rh < n_rh && c == 0) {
-    const int row = (int)(rh / hq), head = (int)(rh % hq);
-    delta[(size_t)head * tq + row] = acc;
-  }
-}
 
 __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float b0, float b1, float b2,
                                       float b3) {
@@ -465,13 +438,31 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
     if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
     const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr];
     lse2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
-    dlt = p.delta[(size_t)head * p.tq + l_row0 + qr];
+    if (p.delta_ready) dlt = p.delta[(size_t)head * p.tq + l_row0 + qr];
   }
   bf16x8 qf[NKS], dof[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     qf[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh) : bf16x8{};
     dof[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.d_o + o_off + 16 * s + 8 * hh) : bf16x8{};
+  }
+  // Delta = rowsum(dO * O) for this row and head, unless the caller supplied
+  // it: this lane's half of the row (d = 16 s + 8 hh .. +8) from the dO
+  // operands already in registers, then the lane pair's sum.  Each (row,
+  // head) belongs to exactly one dQ work item, which stores it for the dK/dV
+  // kernel that runs next.
+  if (!p.delta_ready) {
+    float part = 0.f;
+    if (row_ok) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + o_off + 16 * s + 8 * hh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)ov[e], (float)dof[s][e], part);
+      }
+    }
+    dlt = pair_sum32(part);
+    if (row_ok && hh == 0) p.delta[(size_t)head * p.tq + l_row0 + qr] = dlt;
   }
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -596,29 +587,12 @@ static int dq_heads_per_item(int group) {
 int dq_rows_per_tile(int group) { return 32 * (8 / dq_heads_per_item(group)); }
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t stream) {
-  const long long rh_threads = (long long)p.tq * p.hq * (d / 8);
-  if (rh_threads > 0 && !delta_ready) {
-    const long long blocks = (rh_threads + 255) / 256;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    KernelTimer timer(KC_DELTA, stream);
-    if (d == 128)
-      hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p.o, p.d_o, p.delta,
-                         p.tq, p.hq);
-    else
-      hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p.o, p.d_o, p.delta,
-                         p.tq, p.hq);
-  }
-  const long long nblk_kv = (long long)p.n_kvtiles * p.hkv;
-  if (nblk_kv > 0) {
-    if (nblk_kv > 0x7fffffffLL) return hipErrorInvalidValue;
-    dim3 grid((unsigned)nblk_kv), block(256);
-    KernelTimer timer(KC_DKDV, stream);
-    if (d == 128) hipLaunchKernelGGL((dkdv_kernel<128>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((dkdv_kernel<64>), grid, block, 0, stream, p);
-  }
+  // dQ first: unless the caller supplied Delta, its work items compute and
+  // store it, and the dK/dV kernel reads it
   const int hb = dq_heads_per_item(p.group);
   BwdParams a = p;
   a.n_hb = p.group / hb;
+  a.delta_ready = delta_ready ? 1 : 0;
   const long long nblk_q = (long long)p.n_qtiles_dq * p.hkv * a.n_hb;
   if (nblk_q > 0) {
     if (nblk_q > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -635,6 +609,14 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
       else if (hb == 2) hipLaunchKernelGGL((dq_kernel<64, 4, 2>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((dq_kernel<64, 8, 1>), grid, block, 0, stream, a);
     }
+  }
+  const long long nblk_kv = (long long)p.n_kvtiles * p.hkv;
+  if (nblk_kv > 0) {
+    if (nblk_kv > 0x7fffffffLL) return hipErrorInvalidValue;
+    dim3 grid((unsigned)nblk_kv), block(256);
+    KernelTimer timer(KC_DKDV, stream);
+    if (d == 128) hipLaunchKernelGGL((dkdv_kernel<128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((dkdv_kernel<64>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -65,6 +65,7 @@ struct BwdParams {
   int32_t n_docs, n_qtiles, n_kvtiles, n_qtiles_dq, hq, hkv, group, n_hb, kv_lo, kv_hi, tq;
   int32_t xcd_cluster, xcd_cluster_q;   // ranks per XCD cluster (dK/dV, dQ)
   int32_t accumulate_dq;
+  int32_t delta_ready;    // Delta supplied by the caller (else the dQ kernel computes and stores it)
   float scale;            // softmax scale
   float scale_log2;       // softmax scale * log2(e)
 };

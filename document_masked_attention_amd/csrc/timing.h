@@ -13,7 +13,7 @@ namespace docmask {
 enum KernelClass {
   KC_SCHEDULE = 0,   // validate + tile descriptors + need intervals + LPT orders, per schedule build
   KC_FWD = 1,
-  KC_DELTA = 2,
+  KC_DELTA = 2,      // no separate launch: Delta is formed inside the dQ kernel
   KC_DKDV = 3,
   KC_DQ = 4,
   KC_MERGE = 5,

@@ -128,7 +128,7 @@ const char* docmask_kernel_class_name(int kernel_class) {
   switch (kernel_class) {
     case KC_SCHEDULE: return "schedule";
     case KC_FWD: return "fwd_kernel";
-    case KC_DELTA: return "bwd_delta_kernel";
+    case KC_DELTA: return "delta (computed inside dq_kernel)";
     case KC_DKDV: return "dkdv_kernel";
     case KC_DQ: return "dq_kernel";
     case KC_MERGE: return "merge_kernel";

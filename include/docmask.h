@@ -183,7 +183,7 @@ const char* docmask_strerror(int status);
 enum {
   DOCMASK_KERNEL_SCHEDULE = 0,
   DOCMASK_KERNEL_FWD = 1,
-  DOCMASK_KERNEL_DELTA = 2,
+  DOCMASK_KERNEL_DELTA = 2,     /* never launched: Delta is formed inside the dQ kernel */
   DOCMASK_KERNEL_DKDV = 3,
   DOCMASK_KERNEL_DQ = 4,
   DOCMASK_KERNEL_MERGE = 5,
