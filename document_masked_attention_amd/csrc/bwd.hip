@@ -29,7 +29,6 @@
 //   through LDS transpose reads).
 #include "kernels.h"
 
-#include <cstdlib>
 
 namespace docmask {
 
