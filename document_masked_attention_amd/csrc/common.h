@@ -198,6 +198,15 @@ __device__ __forceinline__ int32_t ld_const(const int32_t* base, size_t idx) {
   return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
 }
 
+// The same 16-byte load from a wave-uniform base (SGPRs) plus a 32-bit lane
+// byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_dma16_s(const void* ubase, uint32_t voff, void* lds_base) {
+  const uint32_t lds_addr =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ubase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Direct 4-byte global-to-LDS load: lane l's dword lands at lds_base + 4 l.
 __device__ __forceinline__ void lds_dma4(const void* gptr, void* lds_base) {
   const uint32_t lds_addr =

@@ -121,19 +121,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     vrow[i] = (uint32_t)(q / VCH) * row_bytes;
     vchk[i] = 16u * (uint32_t)min(q % VCH, CPK - 1);
   }
-  auto issue_k = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
-    const char* tb = reinterpret_cast<const char*>(kbase + (size_t)kt * BK * kv_rstride);
-    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes;
+  // full tiles: uniform tile base + precomputed lane offsets; the ragged last
+  // tile clamps the row part of the offset (a wave-uniform branch)
+  auto issue_rows = [&](const uint16_t* base, int kt, uint16_t* lds, const uint32_t* row, const uint32_t* chk,
+                        auto dp_c, auto wl_c) __attribute__((always_inline)) {
+    constexpr int DP = decltype(dp_c)::value, WL = decltype(wl_c)::value;
+    const uint16_t* tb = base + (size_t)kt * BK * kv_rstride;
+    if ((kt + 1) * BK <= tkv) {
 #pragma unroll
-    for (int i = 0; i < DPK; ++i)
-      if (wave_u + 4 * i < WLK) lds_dma16(tb + min(krow[i], lim) + kchk[i], lds + (wave_u + 4 * i) * 512);
+      for (int i = 0; i < DP; ++i)
+        if (wave_u + 4 * i < WL) lds_dma16_s(tb, row[i] + chk[i], lds + (wave_u + 4 * i) * 512);
+    } else {
+      const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes;
+#pragma unroll
+      for (int i = 0; i < DP; ++i)
+        if (wave_u + 4 * i < WL) lds_dma16_s(tb, min(row[i], lim) + chk[i], lds + (wave_u + 4 * i) * 512);
+    }
+  };
+  auto issue_k = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
+    issue_rows(kbase, kt, lds, krow, kchk, std::integral_constant<int, DPK>{}, std::integral_constant<int, WLK>{});
   };
   auto issue_v = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
-    const char* tb = reinterpret_cast<const char*>(vbase + (size_t)kt * BK * kv_rstride);
-    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes;
-#pragma unroll
-    for (int i = 0; i < DPV; ++i)
-      if (wave_u + 4 * i < WLV) lds_dma16(tb + min(vrow[i], lim) + vchk[i], lds + (wave_u + 4 * i) * 512);
+    issue_rows(vbase, kt, lds, vrow, vchk, std::integral_constant<int, DPV>{}, std::integral_constant<int, WLV>{});
   };
   // transpose-read source address of this lane inside a V tile (see lds_read_tr16)
   const int i16 = lane & 15;
