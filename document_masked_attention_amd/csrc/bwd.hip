@@ -41,6 +41,24 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// S and dP tiles of the dK/dV kernel: v_mfma_f32_32x32x16_bf16 with the
+// accumulator in VGPRs and the B operand (the lane's K or V row) in AGPRs,
+// written as inline assembly so that these tiles stay in VGPRs next to the
+// dK / dV accumulators the compiler keeps in AGPRs (the vector ALU reads them
+// without copies).  The compiler does not see these MFMAs, so it inserts no
+// wait states for them: every vector instruction that reads or writes such a
+// tile is issued at least 12 wait states (issued instructions or s_nop
+// cycles) after the last MFMA that writes it, the latency this 8-pass MFMA
+// needs on gfx950; dP's initial value (-Delta) comes straight from LDS reads.
+__device__ __forceinline__ void mfma_v_zero(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_v_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+// 12 wait states
+__device__ __forceinline__ void mfma_v_settle() { asm volatile("s_nop 7\n\ts_nop 3"); }
+
 // ------------------------------------------------------------------ dK, dV
 // Work item = (KV tile of 128 keys, KV head); four waves of 32 keys, one
 // wave per SIMD.  Each lane keeps one key: its K and V rows are the MFMA B
@@ -61,8 +79,6 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
 // vector ALU while the matrix cores run dV / dK of unit u - 1 and S / dP of
 // unit u + 1.  Two units form a staging step; steps go through a ring of four
 // LDS buffers filled by direct global-to-LDS loads two steps ahead.
-// LSE and Delta read for padded query rows and dummy units: P = 0, dS = 0.
-__device__ const float kBwdPad[2] = {INFINITY, 0.f};
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
@@ -125,75 +141,94 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     // no query row attends this tile: zero gradients
   }
   const int n_steps = (n_units + 1) >> 1;             // the last step may hold one dummy unit
-  auto unit_qt = [&](int u) { return qt_hi - 1 - u / p.group; };
-  auto unit_head = [&](int u) { return kvh * p.group + u % p.group; };
 
-  // this thread's LSE / Delta source and padding word, fixed for the kernel
-  // (kept in registers: a per-lane choice of a parameter inside the loop
-  // would be a vector load whose wait covers the direct loads in flight)
-  const float* ld_src = ((tid >> 6) & 1) ? p.delta : p.lse;
-  const float* ld_pad = &kBwdPad[(tid >> 6) & 1];
-  asm volatile("" : "+v"(ld_src), "+v"(ld_pad));
-  // Plan words of unit u (clamped to the last unit), fetched once per unit
-  // when its step's loads are issued and carried in scalar registers.
+  // LSE (wave 0) or Delta (wave 1) rows staged by this wave; waves 2 and 3
+  // load the same words again, unused, so every wave issues the same number
+  // of vector-memory instructions per step
+  const float* ld_src = (wave & 1) ? p.delta : p.lse;
+  // Unit sequence: unit u is (query block qt_hi - 1 - u / G, head u % G of the
+  // group).  A wave-uniform cursor walks it in order, two units per staged
+  // step; units past the end repeat the last one (dummy units, P = 0).
   struct UnitInfo {
-    int l_row0, g_row0, nrows, head, masked;
+    int l_row0, g_row0, nrows, head, masked, dummy;
   };
-  auto unit_info = [&](int u) __attribute__((always_inline)) -> UnitInfo {
-    u = min(u, n_units - 1);
-    const int qt = unit_qt(u);
+  int cur_u = 0, cur_qt = qt_hi - 1, cur_hd = 0;
+  auto next_unit = [&]() __attribute__((always_inline)) -> UnitInfo {
     UnitInfo ui;
+    ui.dummy = cur_u >= n_units;
+    const int qt = ui.dummy ? qt_lo : cur_qt;
+    ui.head = kvh * p.group + (ui.dummy ? p.group - 1 : cur_hd);
     ui.l_row0 = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_LROW0);
     ui.g_row0 = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_GROW0);
     ui.nrows = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_NROWS);
-    ui.head = unit_head(u);
     // inside the tile's FULL range every (row, key) pair is allowed
     ui.masked = (qt < qt_flo || qt >= qt_fhi || ragged || ui.nrows < BQ) ? 1 : 0;
+    ++cur_u;
+    if (++cur_hd == p.group) { cur_hd = 0; --cur_qt; }
     return ui;
   };
-  // Loads of step s (clamped to the last step; a unit past the end is a
-  // dummy with P = 0) into stage dst, all direct global-to-LDS loads (no
-  // register is written asynchronously): per wave first one dword per lane
-  // into raw[tid] (threads 0..127: LSE then Delta of unit (tid / 32) % 2, row
-  // tid % 32; padded rows, dummy units and threads >= 128 read the padding
-  // constants), then DPW 16-byte loads: load i covers tile t = i / (WLT / 4)
+  // lane byte offsets of the direct loads of a full unit (32 rows): row r of
+  // the tile at r * Hq * D * 2 bytes, chunk position lane % (D/8) holding
+  // chunk chunk_at(r, pos)
+  const uint32_t row_b = (uint32_t)(p.hq * D * sizeof(uint16_t));
+  uint32_t loff_full[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int r = (wave + 4 * (i % (WLT / 4))) * RPL + lane / L::kChunks;
+    loff_full[i] = (uint32_t)r * row_b + 16u * (uint32_t)L::chunk_at(r, lane % L::kChunks);
+  }
+  // Loads of the next step (its two units come back in u0 / u1) into stage
+  // dst, all direct global-to-LDS loads (no register is written
+  // asynchronously): per wave first one dword per lane into raw[tid] (threads
+  // 0..127: LSE then Delta of unit (tid / 32) % 2, row tid % 32 clamped to a
+  // real row), then DPW 16-byte loads: load i covers tile t = i / (WLT / 4)
   // (Q, dO of unit 0, Q, dO of unit 1), rows RPL (wave + 4 (i % (WLT / 4))) ..,
-  // lane -> row + lane / (D/8), chunk position lane % (D/8).
-  // The units' plan words come back in u0 / u1.
-  auto issue = [&](int s, Stage& dst, UnitInfo& u0, UnitInfo& u1) __attribute__((always_inline)) {
-    s = min(s, n_steps - 1);
-    u0 = unit_info(2 * s);
-    u1 = unit_info(2 * s + 1);
+  // lane -> row + lane / (D/8), chunk position lane % (D/8), from the tile's
+  // uniform base plus a 32-bit lane offset.  Units with padded rows clamp the
+  // row to the last real one (one wave-uniform branch).
+  auto issue = [&](Stage& dst, UnitInfo& u0, UnitInfo& u1) __attribute__((always_inline)) {
+    u0 = next_unit();
+    u1 = next_unit();
     {
       const int j = (tid >> 5) & 1, row = tid & 31;
-      const int nrows = j ? u1.nrows : u0.nrows, l_row0 = j ? u1.l_row0 : u0.l_row0;
-      const int head = j ? u1.head : u0.head;
-      const bool dummy = j && (2 * s + 1 >= n_units);
-      const float* src =
-          (tid >= 128 || row >= nrows || dummy) ? ld_pad : ld_src + (size_t)head * p.tq + l_row0 + row;
-      lds_dma4(src, &dst.raw[64 * wave]);
+      const float* b0 = ld_src + (size_t)u0.head * p.tq + u0.l_row0;
+      const float* b1 = ld_src + (size_t)u1.head * p.tq + u1.l_row0;
+      lds_dma4((j ? b1 : b0) + min(row, (j ? u1.nrows : u0.nrows) - 1), &dst.raw[64 * wave]);
     }
-    const int lr = lane / L::kChunks, pos = lane % L::kChunks;
-    static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
-      constexpr int i = decltype(ic)::value;
-      constexpr int t = i / (WLT / 4);
-      const UnitInfo& ui = (t >> 1) ? u1 : u0;
-      const int r0 = (wave + 4 * (i % (WLT / 4))) * RPL;
-      const int r = r0 + lr;
-      const int rr = min(r, ui.nrows - 1);          // padded rows: a real row, never used (P = 0)
-      const size_t off = ((size_t)(ui.l_row0 + rr) * p.hq + ui.head) * D + 8 * L::chunk_at(r, pos);
-      lds_dma16(((t & 1) ? p.d_o : p.q) + off, &dst.qd[t][r0 * D]);
-    });
+    const uint16_t* tb[4] = {p.q + ((size_t)u0.l_row0 * p.hq + u0.head) * D,
+                             p.d_o + ((size_t)u0.l_row0 * p.hq + u0.head) * D,
+                             p.q + ((size_t)u1.l_row0 * p.hq + u1.head) * D,
+                             p.d_o + ((size_t)u1.l_row0 * p.hq + u1.head) * D};
+    if (u0.nrows == BQ && u1.nrows == BQ) {
+      static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int t = i / (WLT / 4);
+        lds_dma16_s(tb[t], loff_full[i], &dst.qd[t][(wave + 4 * (i % (WLT / 4))) * RPL * D]);
+      });
+    } else {
+      static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int t = i / (WLT / 4);
+        const int nrows = (t >> 1) ? u1.nrows : u0.nrows;
+        const int r0 = (wave + 4 * (i % (WLT / 4))) * RPL;
+        const int r = r0 + lane / L::kChunks;
+        const uint32_t off =
+            (uint32_t)min(r, nrows - 1) * row_b + 16u * (uint32_t)L::chunk_at(r, lane % L::kChunks);
+        lds_dma16_s(tb[t], off, &dst.qd[t][r0 * D]);
+      });
+    }
   };
-  // LSE2 / -Delta of a staged step, from this thread's own loaded word
-  // (padded rows and dummy units read LSE = +inf, Delta = 0: P = 0; an empty
-  // row, LSE = -inf, likewise gets P = 0)
-  auto finish = [&](Stage& dst) __attribute__((always_inline)) {
+  // LSE2 / -Delta of a staged step, from this thread's own loaded word:
+  // padded rows and dummy units get LSE = +inf, Delta = 0 (P = 0); an empty
+  // row (LSE = -inf) likewise gets P = 0
+  auto finish = [&](Stage& dst, const UnitInfo& u0, const UnitInfo& u1) __attribute__((always_inline)) {
     const float v = dst.raw[tid];
+    const int j = (tid >> 5) & 1, row = tid & 31;
+    const bool pad = row >= (j ? u1.nrows : u0.nrows) || (j ? u1.dummy : u0.dummy);
     if (tid < 64) {
-      dst.lse[tid >> 5][tid & 31] = v == -INFINITY ? INFINITY : v * kLog2e;
+      dst.lse[j][row] = (pad || v == -INFINITY) ? INFINITY : v * kLog2e;
     } else if (tid < 128) {
-      dst.ndl[(tid >> 5) & 1][tid & 31] = -v;
+      dst.ndl[j][row] = pad ? 0.f : -v;
     }
   };
   // waits until at most `n` of this wave's vector-memory instructions are
@@ -215,6 +250,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     const int lo = key_g - ui.g_row0;
     const int hi = key_ok ? min(key_end - ui.g_row0, ui.nrows) : lo;
     const unsigned span = (unsigned)max(hi - lo, 0);
+    mfma_v_settle();
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if ((unsigned)(8 * (e >> 2) + 4 * hh + (e & 3) - lo) >= span) sa[e] = -INFINITY;
@@ -268,10 +304,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       if constexpr (k + PF < NP) load(std::integral_constant<int, k + PF>{});
       if constexpr (k % 2 == 0) {
         dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], pba[t], dvacc[m], 0, 0, 0);
-        sab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], kf[sb], sb == 0 ? f32x16{} : sab, 0, 0, 0);
+        if constexpr (sb == 0) mfma_v_zero(sab, opb[k], kf[sb]); else mfma_v_acc(sab, opb[k], kf[sb]);
       } else {
         dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], dsba[t], dkacc[m], 0, 0, 0);
-        dab = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[k], vf[sb], sb == 0 ? ndb : dab, 0, 0, 0);
+        if constexpr (sb == 0) dab = ndb;
+        mfma_v_acc(dab, opb[k], vf[sb]);
       }
       static_for<EPS>([&](auto ec) __attribute__((always_inline)) {
         constexpr int e = k * EPS + decltype(ec)::value;
@@ -308,9 +345,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       const int off = L::off(l32, 16 * s + 8 * hh);
       const bf16x8 qa_ = *reinterpret_cast<const bf16x8*>(&qs[off]);
       const bf16x8 da_ = *reinterpret_cast<const bf16x8*>(&dos[off]);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kf[s], s == 0 ? f32x16{} : sa, 0, 0, 0);
-      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da_, vf[s], s == 0 ? nd : da, 0, 0, 0);
+      if (s == 0) {
+        mfma_v_zero(sa, qa_, kf[s]);
+        da = nd;
+      } else {
+        mfma_v_acc(sa, qa_, kf[s]);
+      }
+      mfma_v_acc(da, da_, vf[s]);
     }
+    mfma_v_settle();
   };
   // dV^T += dO^T P and dK^T += Q^T dS for unit j of stage cur, alone (pipeline end)
   auto dvdk = [&](const Stage& cur, int j, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2])
@@ -334,16 +377,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   if (n_units > 0) {
     // prologue: steps 0 and 1 staged; S / dP of unit 0
     UnitInfo ic0, ic1, in0, in1;      // plan words of steps s and s + 1
-    issue(0, st[0], ic0, ic1);
-    issue(1, st[1], in0, in1);
+    issue(st[0], ic0, ic1);
+    issue(st[1], in0, in1);
     wait_vm(std::integral_constant<int, 0>{});
-    finish(st[0]);
-    finish(st[1]);
+    finish(st[0], ic0, ic1);
+    finish(st[1], in0, in1);
     // the key's document end and the K / V operands are in registers before
     // any later loads are in flight
     asm volatile("" ::"v"(key_end));
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
+    for (int s = 0; s < NKS; ++s) asm volatile("" ::"a"(kf[s]), "a"(vf[s]));
     __syncthreads();
 
     f32x16 sa[2], da[2];
@@ -359,14 +402,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       Stage& nx2 = st[(s + 2) & (NBUF - 1)];
       // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
       UnitInfo i20, i21;
-      issue(s + 2, nx2, i20, i21);
+      issue(nx2, i20, i21);
       __builtin_amdgcn_sched_barrier(0);
       region(s == 0 ? cur : prv, 1, pb[1], dsb[1], cur, 1, sa[1], da[1], cur, 0, sa[0], da[0], pb[0], dsb[0]);
       if (ic1.masked) unit_mask(ic1, sa[1]);
       // ---- step s + 1 staged (its loads were issued two regions ago)
       if (s > 0) {
         wait_vm(std::integral_constant<int, VM_PER_STEP>{});
-        finish(nx1);
+        finish(nx1, in0, in1);
       }
       __syncthreads();
       // ---- region 2s + 1: dV, dK (2s) | S, dP (2s + 2) | softmax(2s + 1)
