@@ -509,6 +509,10 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int b = 0; b < NDB; ++b) dqacc[b] = f32x16{};
+  // -Delta of this lane's row in every accumulator entry: the initial dP^T
+  f32x16 ndlt;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndlt[r] = -dlt;
 
   const int tkv = p.kv_hi - p.kv_lo;
   const size_t kv_rstride = (size_t)p.hkv * D;
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
     const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      f32x16 sacc = f32x16{}, dpacc = ndlt;          // dP^T starts from -Delta: dS^T = P^T dP^T
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[L::off(32 * kb + ln, 16 * s + 8 * hh)]);
@@ -583,7 +587,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse2));
-        ds[r] = pr * (dpacc[r] - dlt);
+        ds[r] = pr * dpacc[r];
       }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
