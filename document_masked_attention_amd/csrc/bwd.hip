@@ -297,7 +297,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       for (int r = 0; r < 4; ++r) ndb[4 * jj + r] = d4[r];
     }
     static_for<PF>([&](auto kc) __attribute__((always_inline)) { load(kc); });
-    float pv[16], dsv[16];
+    float xv[16], pv[16], dsv[16];
+    static_for<EPS>([&](auto ec) __attribute__((always_inline)) {
+      constexpr int e = decltype(ec)::value;
+      xv[e] = __builtin_fmaf(sac[e], p.scale_log2, -l4[e / 4][e % 4]);
+    });
     static_for<NP>([&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
       constexpr int m = k / 4, t = (k / 2) % 2, sb = k / 2;
@@ -310,14 +314,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         if constexpr (sb == 0) dab = ndb;
         mfma_v_acc(dab, opb[k], vf[sb]);
       }
+      // softmax elements, software-pipelined across slots so that no
+      // instruction waits on one issued just before it: slot k forms the
+      // exponent argument of its next slot's elements, exponentiates its own
+      // and multiplies the previous slot's by dP
       static_for<EPS>([&](auto ec) __attribute__((always_inline)) {
         constexpr int e = k * EPS + decltype(ec)::value;
-        const float pe =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(sac[e], p.scale_log2, -l4[e / 4][e % 4]));
-        pv[e] = pe;
-        dsv[e] = pe * dac[e];
+        if constexpr (e + EPS < 16) xv[e + EPS] = __builtin_fmaf(sac[e + EPS], p.scale_log2, -l4[(e + EPS) / 4][(e + EPS) % 4]);
+        pv[e] = __builtin_amdgcn_exp2f(xv[e]);
+        if constexpr (e >= EPS) dsv[e - EPS] = pv[e - EPS] * dac[e - EPS];
       });
       __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<EPS>([&](auto ec) __attribute__((always_inline)) {
+      constexpr int e = 16 - EPS + decltype(ec)::value;
+      dsv[e] = pv[e] * dac[e];
     });
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
