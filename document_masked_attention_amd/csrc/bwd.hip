@@ -577,6 +577,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
     const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // MFMA phases at raised wave priority (the other wave of the SIMD fills
+      // the gaps with its vector work)
+      __builtin_amdgcn_s_setprio(1);
       f32x16 sacc = f32x16{}, dpacc = ndlt;          // dP^T starts from -Delta: dS^T = P^T dP^T
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
@@ -585,6 +588,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc, 0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // document mask (PARTIAL and ragged tiles only, a wave-uniform branch):
       // masked scores become -inf, so P = 0
       if (partial) {
@@ -600,6 +604,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse2));
         ds[r] = pr * dpacc[r];
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const bf16x8 dsb = cvt8(ds[8 * k2], ds[8 * k2 + 1], ds[8 * k2 + 2], ds[8 * k2 + 3], ds[8 * k2 + 4],
@@ -612,6 +617,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     store_k(k_s[buf ^ 1], kr);
     store_v(v_s[buf ^ 1], vr);
     __syncthreads();

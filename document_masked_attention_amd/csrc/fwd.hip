@@ -236,7 +236,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       }
     l_run += rs;
     // S of the next tile, into the registers this tile's softmax has just
-    // read; those MFMAs and this tile's PV run back to back
+    // read; those MFMAs and this tile's PV run back to back, at raised wave
+    // priority so that the matrix core is fed first while the other wave of
+    // the SIMD runs its softmax
+    __builtin_amdgcn_s_setprio(1);
     if (has_next) compute_s(k_lds[(u + 1) & 1], s_cur);
 
     // O^T += V^T P^T, 16 keys per step; V^T comes from the row-major V tile
@@ -250,6 +253,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         const bf16x8 vf = tr_operand(vp, vp + 8 * VSTR);
         oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[b], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) {
       wait_vmem();
       __syncthreads();
