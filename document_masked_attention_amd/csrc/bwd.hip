@@ -93,13 +93,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   constexpr int WLT = BQ / RPL;         // direct loads per tile
   constexpr int DPW = 4 * WLT / 4;      // direct loads per wave per step (2 units x Q, dO = 4 tiles)
   constexpr int VM_PER_STEP = 1 + DPW;  // vector-memory instructions per wave per step
-  struct Stage {
-    uint16_t qd[4][TE];     // [2 j + 0: Q, 2 j + 1: dO] of unit j of the step
+  constexpr int TB = 2 * TE;            // bytes per Q / dO tile
+  constexpr int QDB = 4 * TB;           // bytes per staging step of tiles
+  // Q / dO tiles of the ring: qd[g][2 j + 0: Q, 2 j + 1: dO] of unit j of the
+  // step staged in buffer g; their LSE / Delta rows in sm[g]
+  struct Small {
     float lse[2][BQ];       // LSE * log2(e); +inf: P = 0
     float ndl[2][BQ];       // -Delta
     float raw[256];         // loaded LSE / Delta words, one per thread
   };
-  __shared__ __attribute__((aligned(16))) Stage st[NBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t qd[NBUF][4][TE];
+  __shared__ __attribute__((aligned(16))) Small sm[NBUF];
 
   if (p.err[0]) return;
 
@@ -186,14 +190,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // lane -> row + lane / (D/8), chunk position lane % (D/8), from the tile's
   // uniform base plus a 32-bit lane offset.  Units with padded rows clamp the
   // row to the last real one (one wave-uniform branch).
-  auto issue = [&](Stage& dst, UnitInfo& u0, UnitInfo& u1) __attribute__((always_inline)) {
+  auto issue = [&](int g, UnitInfo& u0, UnitInfo& u1) __attribute__((always_inline)) {
     u0 = next_unit();
     u1 = next_unit();
     {
       const int j = (tid >> 5) & 1, row = tid & 31;
       const float* b0 = ld_src + (size_t)u0.head * p.tq + u0.l_row0;
       const float* b1 = ld_src + (size_t)u1.head * p.tq + u1.l_row0;
-      lds_dma4((j ? b1 : b0) + min(row, (j ? u1.nrows : u0.nrows) - 1), &dst.raw[64 * wave]);
+      lds_dma4((j ? b1 : b0) + min(row, (j ? u1.nrows : u0.nrows) - 1), &sm[g].raw[64 * wave]);
     }
     const uint16_t* tb[4] = {p.q + ((size_t)u0.l_row0 * p.hq + u0.head) * D,
                              p.d_o + ((size_t)u0.l_row0 * p.hq + u0.head) * D,
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         constexpr int t = i / (WLT / 4);
-        lds_dma16_s(tb[t], loff_full[i], &dst.qd[t][(wave + 4 * (i % (WLT / 4))) * RPL * D]);
+        lds_dma16_s(tb[t], loff_full[i], &qd[g][t][(wave + 4 * (i % (WLT / 4))) * RPL * D]);
       });
     } else {
       static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
@@ -214,14 +218,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         const int r = r0 + lane / L::kChunks;
         const uint32_t off =
             (uint32_t)min(r, nrows - 1) * row_b + 16u * (uint32_t)L::chunk_at(r, lane % L::kChunks);
-        lds_dma16_s(tb[t], off, &dst.qd[t][r0 * D]);
+        lds_dma16_s(tb[t], off, &qd[g][t][r0 * D]);
       });
     }
   };
   // LSE2 / -Delta of a staged step, from this thread's own loaded word:
   // padded rows and dummy units get LSE = +inf, Delta = 0 (P = 0); an empty
   // row (LSE = -inf) likewise gets P = 0
-  auto finish = [&](Stage& dst, const UnitInfo& u0, const UnitInfo& u1) __attribute__((always_inline)) {
+  auto finish = [&](int g, const UnitInfo& u0, const UnitInfo& u1) __attribute__((always_inline)) {
+    Small& dst = sm[g];
     const float v = dst.raw[tid];
     const int j = (tid >> 5) & 1, row = tid & 31;
     const bool pad = row >= (j ? u1.nrows : u0.nrows) || (j ? u1.dummy : u0.dummy);
@@ -241,6 +246,43 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // the k-step (second read: + 8), column 16 ((lane / 16) % 2) + 4 (lane % 4)
   // of the 32-wide d block
   const int tr_row = 4 * hh + ((lane >> 2) & 3), tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // LDS reads of the ring use a lane byte offset inside a tile held in a
+  // register plus a constant (buffer, tile, k-step) in the instruction's
+  // 16-bit offset field; buffers at or above 64 KiB use a second copy of the
+  // lane offsets advanced by 64 KiB.  Row reads: row l32, k-step sb.
+  // Transpose reads: d block m, rows tr_row (+ 8); the 16-row k-step t of a
+  // tile adds 16 rows (the swizzle repeats every 16 rows).
+  const char* qd_b = reinterpret_cast<const char*>(&qd[0][0][0]);
+  constexpr bool kTwoSets = NBUF * QDB > 65536;
+  uint32_t ro_lo[NKS], ro_hi[NKS], tro_lo[NMB][2], tro_hi[NMB][2];
+#pragma unroll
+  for (int sb = 0; sb < NKS; ++sb) {
+    ro_lo[sb] = 2u * (uint32_t)L::off(l32, 16 * sb + 8 * hh);
+    ro_hi[sb] = ro_lo[sb] + 65536u;
+  }
+#pragma unroll
+  for (int m = 0; m < NMB; ++m)
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      tro_lo[m][o] = 2u * (uint32_t)L::off(8 * o + tr_row, 32 * m + tr_col);
+      tro_hi[m][o] = tro_lo[m][o] + 65536u;
+    }
+  if constexpr (kTwoSets) {
+    // separate registers (no re-adding of 64 KiB per read); the mask keeps
+    // the values known non-negative so that constants fold into the offset
+#pragma unroll
+    for (int sb = 0; sb < NKS; ++sb) { asm volatile("" : "+v"(ro_hi[sb])); ro_hi[sb] &= 0x3ffffu; }
+#pragma unroll
+    for (int m = 0; m < NMB; ++m)
+#pragma unroll
+      for (int o = 0; o < 2; ++o) { asm volatile("" : "+v"(tro_hi[m][o])); tro_hi[m][o] &= 0x3ffffu; }
+  }
+  // address of buffer G, tile T, constant byte offset C, lane offset (lo, hi)
+  auto qd_at = [&](auto g_c, auto t_c, auto c_c, uint32_t lo, uint32_t hi) __attribute__((always_inline)) {
+    constexpr uint32_t off = decltype(g_c)::value * QDB + decltype(t_c)::value * TB + decltype(c_c)::value;
+    if constexpr (!kTwoSets || off < 65536u - TB) return reinterpret_cast<const uint16_t*>(qd_b + lo + off);
+    else return reinterpret_cast<const uint16_t*>(qd_b + hi + (off - 65536u));
+  };
 
   // document mask of a unit on its S accumulators: scores of (row, this key)
   // pairs that are not allowed become -inf (P = 0).  Only units outside the
@@ -267,25 +309,28 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   constexpr int NP = 4 * NMB;           // == 2 * NKS: slots per region
   constexpr int PF = 3;                 // operand prefetch distance (slots)
   constexpr int EPS = 16 / NP;          // softmax elements per slot
-  auto region = [&](const Stage& sta, int ja, const bf16x8 (&pba)[2], const bf16x8 (&dsba)[2],
-                    const Stage& stb, int jb, f32x16& sab, f32x16& dab,
-                    const Stage& stc, int jc, const f32x16& sac, const f32x16& dac, bf16x8 (&pbc)[2],
+  // Buffers GA (unit ja: dV / dK operands), GB (unit jb: S / dP operands)
+  // and GC (unit jc: softmax LSE) are compile-time ring indices.
+  auto region = [&](auto ga_c, auto ja_c, const bf16x8 (&pba)[2], const bf16x8 (&dsba)[2],
+                    auto gb_c, auto jb_c, f32x16& sab, f32x16& dab,
+                    auto gc_c, auto jc_c, const f32x16& sac, const f32x16& dac, bf16x8 (&pbc)[2],
                     bf16x8 (&dsbc)[2]) __attribute__((always_inline)) {
-    const uint16_t* a_q = sta.qd[2 * ja];
-    const uint16_t* a_do = sta.qd[2 * ja + 1];
-    const uint16_t* b_q = stb.qd[2 * jb];
-    const uint16_t* b_do = stb.qd[2 * jb + 1];
+    constexpr int ja = decltype(ja_c)::value, jb = decltype(jb_c)::value, jc = decltype(jc_c)::value;
+    using IC = std::integral_constant<int, 0>;
     bf16x8 opa[NP], opb[NP];
     auto load = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
       constexpr int m = k / 4, t = (k / 2) % 2, sb = k / 2;
-      const int o0 = L::off(16 * t + tr_row, 32 * m + tr_col);
-      const int o1 = L::off(16 * t + 8 + tr_row, 32 * m + tr_col);
-      const uint16_t* ta = (k % 2) ? a_q : a_do;
-      opa[k] = tr_operand(ta + o0, ta + o1);
-      const uint16_t* tb = (k % 2) ? b_do : b_q;
-      opb[k] = *reinterpret_cast<const bf16x8*>(&tb[L::off(l32, 16 * sb + 8 * hh)]);
+      // A: dO^T (k even) or Q^T (k odd) of unit ja; B: Q (k even) or dO (k odd) rows of unit jb
+      using TA = std::integral_constant<int, 2 * ja + 1 - (k % 2)>;
+      using TBt = std::integral_constant<int, 2 * jb + (k % 2)>;
+      using CT = std::integral_constant<int, 16 * t * D * 2>;
+      opa[k] = tr_operand(qd_at(ga_c, TA{}, CT{}, tro_lo[m][0], tro_hi[m][0]),
+                          qd_at(ga_c, TA{}, CT{}, tro_lo[m][1], tro_hi[m][1]));
+      opb[k] = *reinterpret_cast<const bf16x8*>(qd_at(gb_c, TBt{}, IC{}, ro_lo[sb], ro_hi[sb]));
     };
+    const Small& stc = sm[decltype(gc_c)::value];
+    const Small& stb = sm[decltype(gb_c)::value];
     f32x4 l4[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) l4[jj] = *reinterpret_cast<const f32x4*>(&stc.lse[jc][8 * jj + 4 * hh]);
@@ -340,14 +385,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     asm volatile("" : "+v"(pbc[0]), "+v"(pbc[1]), "+v"(dsbc[0]), "+v"(dsbc[1]));
     __builtin_amdgcn_sched_barrier(0);
   };
-  // S and dP (from -Delta) of unit j of stage cur, alone (pipeline start)
-  auto sdp = [&](const Stage& cur, int j, f32x16& sa, f32x16& da) __attribute__((always_inline)) {
-    const uint16_t* qs = cur.qd[2 * j];
-    const uint16_t* dos = cur.qd[2 * j + 1];
+  // S and dP (from -Delta) of unit j of buffer g, alone (pipeline start)
+  auto sdp = [&](int g, int j, f32x16& sa, f32x16& da) __attribute__((always_inline)) {
+    const uint16_t* qs = qd[g][2 * j];
+    const uint16_t* dos = qd[g][2 * j + 1];
     f32x16 nd;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cur.ndl[j][8 * jj + 4 * hh]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm[g].ndl[j][8 * jj + 4 * hh]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) nd[4 * jj + r] = d4[r];
     }
@@ -366,11 +411,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     }
     mfma_v_settle();
   };
-  // dV^T += dO^T P and dK^T += Q^T dS for unit j of stage cur, alone (pipeline end)
-  auto dvdk = [&](const Stage& cur, int j, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2])
-      __attribute__((always_inline)) {
-    const uint16_t* qs = cur.qd[2 * j];
-    const uint16_t* dos = cur.qd[2 * j + 1];
+  // dV^T += dO^T P and dK^T += Q^T dS for unit j of buffer g, alone (pipeline end)
+  auto dvdk = [&](int g, int j, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+    const uint16_t* qs = qd[g][2 * j];
+    const uint16_t* dos = qd[g][2 * j + 1];
 #pragma unroll
     for (int m = 0; m < NMB; ++m) {
 #pragma unroll
@@ -386,13 +430,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   };
 
   if (n_units > 0) {
-    // prologue: steps 0 and 1 staged; S / dP of unit 0
+    // prologue: steps 0 and 1 staged; S / dP of unit 0.  Unit 1's tiles of
+    // buffer NBUF - 1 (the operands of the "previous unit" of step 0, whose P
+    // and dS are zero) are cleared, so that 0 * garbage cannot make a NaN.
     UnitInfo ic0, ic1, in0, in1;      // plan words of steps s and s + 1
-    issue(st[0], ic0, ic1);
-    issue(st[1], in0, in1);
+    issue(0, ic0, ic1);
+    issue(1, in0, in1);
+    {
+      uint4* z = reinterpret_cast<uint4*>(&qd[NBUF - 1][2][0]);
+#pragma unroll
+      for (int i = 0; i < 2 * TB / 16 / 256; ++i) z[tid + 256 * i] = uint4{0u, 0u, 0u, 0u};
+    }
     wait_vm(std::integral_constant<int, 0>{});
-    finish(st[0], ic0, ic1);
-    finish(st[1], in0, in1);
+    finish(0, ic0, ic1);
+    finish(1, in0, in1);
     // the key's document end and the K / V operands are in registers before
     // any later loads are in flight
     asm volatile("" ::"v"(key_end));
@@ -404,33 +455,44 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     bf16x8 pb[2][2], dsb[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) { pb[1][t] = bf16x8{}; dsb[1][t] = bf16x8{}; }   // unit -1: adds zero
-    sdp(st[0], 0, sa[0], da[0]);
+    sdp(0, 0, sa[0], da[0]);
     if (ic0.masked) unit_mask(ic0, sa[0]);
-    for (int s = 0; s < n_steps; ++s) {
-      Stage& cur = st[s & (NBUF - 1)];
-      Stage& prv = st[(s + NBUF - 1) & (NBUF - 1)];      // unit 2s - 1 (s = 0: zero operands on stage 0)
-      Stage& nx1 = st[(s + 1) & (NBUF - 1)];
-      Stage& nx2 = st[(s + 2) & (NBUF - 1)];
+    // Step s (buffer phase PH = s mod NBUF, a compile-time constant so that
+    // every LDS address is a register plus an immediate): units 2s, 2s + 1.
+    auto step = [&](int s, auto ph_c) __attribute__((always_inline)) {
+      constexpr int ph = decltype(ph_c)::value;
+      using GC = std::integral_constant<int, ph>;
+      using GP = std::integral_constant<int, (ph + NBUF - 1) % NBUF>;
+      using GN1 = std::integral_constant<int, (ph + 1) % NBUF>;
+      using J0 = std::integral_constant<int, 0>;
+      using J1 = std::integral_constant<int, 1>;
       // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
       UnitInfo i20, i21;
-      issue(nx2, i20, i21);
+      issue((ph + 2) % NBUF, i20, i21);
       __builtin_amdgcn_sched_barrier(0);
-      region(s == 0 ? cur : prv, 1, pb[1], dsb[1], cur, 1, sa[1], da[1], cur, 0, sa[0], da[0], pb[0], dsb[0]);
+      region(GP{}, J1{}, pb[1], dsb[1], GC{}, J1{}, sa[1], da[1], GC{}, J0{}, sa[0], da[0], pb[0], dsb[0]);
       if (ic1.masked) unit_mask(ic1, sa[1]);
       // ---- step s + 1 staged (its loads were issued two regions ago)
       if (s > 0) {
         wait_vm(std::integral_constant<int, VM_PER_STEP>{});
-        finish(nx1, in0, in1);
+        finish(GN1::value, in0, in1);
       }
       __syncthreads();
       // ---- region 2s + 1: dV, dK (2s) | S, dP (2s + 2) | softmax(2s + 1)
       __builtin_amdgcn_sched_barrier(0);
-      region(cur, 0, pb[0], dsb[0], nx1, 0, sa[0], da[0], cur, 1, sa[1], da[1], pb[1], dsb[1]);
+      region(GC{}, J0{}, pb[0], dsb[0], GN1{}, J0{}, sa[0], da[0], GC{}, J1{}, sa[1], da[1], pb[1], dsb[1]);
       if (in0.masked) unit_mask(in0, sa[0]);
       ic0 = in0; ic1 = in1; in0 = i20; in1 = i21;
+    };
+    static_assert(NBUF == 4, "one unrolled step per buffer phase");
+    for (int s = 0; s < n_steps; s += NBUF) {
+      step(s, std::integral_constant<int, 0>{});
+      if (s + 1 < n_steps) step(s + 1, std::integral_constant<int, 1>{});
+      if (s + 2 < n_steps) step(s + 2, std::integral_constant<int, 2>{});
+      if (s + 3 < n_steps) step(s + 3, std::integral_constant<int, 3>{});
     }
     // the last unit's dV, dK (a dummy unit adds zero)
-    dvdk(st[(n_steps - 1) & (NBUF - 1)], 1, pb[1], dsb[1]);
+    dvdk((n_steps - 1) & (NBUF - 1), 1, pb[1], dsb[1]);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads
   }
 
