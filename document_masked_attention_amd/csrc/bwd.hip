@@ -628,13 +628,27 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
     store_v(v_s[0], vr);
   }
   __syncthreads();
-  for (int u = 0; u < n; ++u) {
+  // K reads: a lane byte offset inside the tile (row ln or kt_row (+ 8),
+  // column block) plus a constant (buffer, 32-key block, 16-key step) in the
+  // instruction's offset field; the swizzle repeats every 16 rows
+  constexpr int KRB = L::kRowElems * 2;                 // bytes per K row
+  const char* kb_s = reinterpret_cast<const char*>(&k_s[0][0]);
+  uint32_t ko[NKS], kto[NDB][2];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) ko[s] = 2u * (uint32_t)L::off(ln, 16 * s + 8 * hh);
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int o = 0; o < 2; ++o) kto[b][o] = 2u * (uint32_t)L::off(kt_row + 8 * o, 32 * b + kt_col);
+  // One KV tile (index u); the K / V buffer is a compile-time constant so
+  // that LDS addresses fold into immediates.
+  auto tile_step = [&](int u, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int KB0 = buf * L::kElems(BK) * 2;          // byte offset of this K buffer
     const int kt = kt_lo + u;
-    const int buf = u & 1;
     u32x4 kr[KPASS], vr[KPASS];
     load_rows(kbase, min(kt + 1, kt_hi - 1), kr);    // the last tile again on the final step
     load_rows(vbase, min(kt + 1, kt_hi - 1), vr);
-    const uint16_t* ks = k_s[buf];
     const uint16_t* vs = v_s[buf];
     const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
 #pragma unroll
@@ -645,7 +659,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
       f32x16 sacc = f32x16{}, dpacc = ndlt;          // dP^T starts from -Delta: dS^T = P^T dP^T
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[L::off(32 * kb + ln, 16 * s + 8 * hh)]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb_s + ko[s] + (KB0 + 32 * kb * KRB));
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[(32 * kb + ln) * VS + 16 * s + 8 * hh]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc, 0, 0, 0);
@@ -673,8 +687,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
                                 ds[8 * k2 + 5], ds[8 * k2 + 6], ds[8 * k2 + 7]);
 #pragma unroll
         for (int b = 0; b < NDB; ++b) {
-          const int r0 = 32 * kb + 16 * k2 + kt_row;
-          const bf16x8 kT = tr_operand(ks + L::off(r0, 32 * b + kt_col), ks + L::off(r0 + 8, 32 * b + kt_col));
+          const int rows_b = (32 * kb + 16 * k2) * KRB;
+          const bf16x8 kT = tr_operand(reinterpret_cast<const uint16_t*>(kb_s + kto[b][0] + (KB0 + rows_b)),
+                                       reinterpret_cast<const uint16_t*>(kb_s + kto[b][1] + (KB0 + rows_b)));
           dqacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsb, dqacc[b], 0, 0, 0);
         }
       }
@@ -683,6 +698,10 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
     store_k(k_s[buf ^ 1], kr);
     store_v(v_s[buf ^ 1], vr);
     __syncthreads();
+  };
+  for (int u = 0; u < n; u += 2) {
+    tile_step(u, std::integral_constant<int, 0>{});
+    if (u + 1 < n) tile_step(u + 1, std::integral_constant<int, 1>{});
   }
 
   // dQ = scale * acc: lane's row, d = 32 b + 8 g + 4 hh .. +4 (added to dq for split-KV callers)
