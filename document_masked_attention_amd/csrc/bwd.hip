@@ -350,12 +350,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     static_for<NP>([&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
       constexpr int m = k / 4, t = (k / 2) % 2, sb = k / 2;
-      if constexpr (k + PF < NP) load(std::integral_constant<int, k + PF>{});
-      if constexpr (k % 2 == 0) {
+      if constexpr (k % 2 == 0)
         dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], pba[t], dvacc[m], 0, 0, 0);
+      else
+        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], dsba[t], dkacc[m], 0, 0, 0);
+      if constexpr (k + PF < NP) load(std::integral_constant<int, k + PF>{});
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (k % 2 == 0) {
         if constexpr (sb == 0) mfma_v_zero(sab, opb[k], kf[sb]); else mfma_v_acc(sab, opb[k], kf[sb]);
       } else {
-        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[k], dsba[t], dkacc[m], 0, 0, 0);
         if constexpr (sb == 0) dab = ndb;
         mfma_v_acc(dab, opb[k], vf[sb]);
       }
