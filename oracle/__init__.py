@@ -31,11 +31,12 @@ force, finite differences, hand-derived fixtures in ``tests/golden/``).
 """
 from .attention import (doc_index, local_positions, allowed_mask, attention_forward,
                         attention_backward, lse_merge)
+from .convert import round_to_bf16_bits
 from .schedule import (q_tiles, kv_tiles, tile_pair_counts_bruteforce, tile_pair_counts,
                        classify, schedule, need_intervals, useful_pairs, lpt_order)
 
 __all__ = [
     "doc_index", "local_positions", "allowed_mask", "attention_forward", "attention_backward",
     "lse_merge", "q_tiles", "kv_tiles", "tile_pair_counts_bruteforce", "tile_pair_counts",
-    "classify", "schedule", "need_intervals", "useful_pairs", "lpt_order",
+    "classify", "schedule", "need_intervals", "useful_pairs", "lpt_order", "round_to_bf16_bits",
 ]
