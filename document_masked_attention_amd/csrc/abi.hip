@@ -70,8 +70,8 @@ ChunkTable make_table(const docmask_chunk* chunks, int32_t n_chunks) {
 
 // Workspace layout of one entry point (byte offsets; 0 = region absent).
 struct Layout {
-  size_t plan_q = 0, key_q = 0, lpt_q = 0, kvdesc = 0, key_kv = 0, lpt_kv = 0, plan_q2 = 0, hist = 0, delta = 0,
-         total = 0;
+  size_t plan_q = 0, key_q = 0, lpt_q = 0, kvdesc = 0, key_kv = 0, lpt_kv = 0, kv_pair = 0, key_pair = 0, plan_q2 = 0,
+         hist = 0, delta = 0, total = 0;
   int64_t n_qt = 0, n_kt = 0, n_qt2 = 0, n_kt2 = 0;
 };
 
@@ -101,10 +101,12 @@ Layout bwd_layout(const docmask_chunk* chunks, int32_t n_chunks, const Problem& 
   L.kvdesc = off; off = align_up(off + (size_t)L.n_kt * 4 * 4);
   L.key_kv = off; off = align_up(off + (size_t)L.n_kt * 4);
   L.lpt_kv = off; off = align_up(off + (size_t)L.n_kt * 4);
+  L.kv_pair = off; off = align_up(off + (size_t)L.n_kt * 4);
+  L.key_pair = off; off = align_up(off + (size_t)L.n_kt * 4);
   L.plan_q2 = off; off = align_up(off + (size_t)L.n_qt2 * QP_WORDS * 4);
   L.key_q = off;  off = align_up(off + (size_t)L.n_qt2 * 4);
   L.lpt_q = off;  off = align_up(off + (size_t)L.n_qt2 * 4);
-  const int64_t hist_n = (L.n_qt > L.n_kt2 ? L.n_qt : L.n_kt2) + 1;
+  const int64_t hist_n = (L.n_qt > L.n_kt2 ? L.n_qt : L.n_kt2) + 2;
   L.hist = off;   off = align_up(off + (size_t)hist_n * 4);
   L.delta = off;  off = align_up(off + (size_t)hq * pr.tq * 4);
   L.total = off;
@@ -259,6 +261,8 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   sp.plan_q = at<int32_t>(workspace, L.plan_q);
   sp.kvdesc = at<int32_t>(workspace, L.kvdesc);
   sp.key_kv = at<int32_t>(workspace, L.key_kv);
+  sp.kv_pair = at<int32_t>(workspace, L.kv_pair);
+  sp.key_pair = at<int32_t>(workspace, L.key_pair);
   sp.err = at<int32_t>(workspace, 0);
   int32_t* lpt_kv = at<int32_t>(workspace, L.lpt_kv);
   hipError_t e = launch_schedule(sp, nullptr, lpt_kv, at<int32_t>(workspace, L.hist), stream);
@@ -270,6 +274,8 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   sq.plan_q = at<int32_t>(workspace, L.plan_q2);
   sq.kvdesc = nullptr;
   sq.key_kv = nullptr;
+  sq.kv_pair = nullptr;
+  sq.key_pair = nullptr;
   sq.key_q = at<int32_t>(workspace, L.key_q);
   int32_t* lpt_q = at<int32_t>(workspace, L.lpt_q);
   e = launch_schedule(sq, lpt_q, nullptr, at<int32_t>(workspace, L.hist), stream);
@@ -289,6 +295,7 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   bp.plan_kq = sp.plan_q;
   bp.kvdesc = sp.kvdesc;
   bp.lpt_kv = lpt_kv;
+  bp.kv_pair = sp.kv_pair;
   bp.plan_q = sq.plan_q;
   bp.lpt_q = lpt_q;
   bp.err = sp.err;

@@ -107,60 +107,46 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 
   if (p.err[0]) return;
 
+  // Work item: a pair of KV tiles (the lower one leads; the scheduler's
+  // pairing), or one tile alone; a tile that is not a leader runs inside its
+  // leader's work item.
   const WorkItem wi = map_work(blockIdx.x, p.n_kvtiles, p.hkv, 1, p.xcd_cluster);
   const int kvh = wi.kvh;
-  const int tile = min(max(ld_const(p.lpt_kv, wi.rank), 0), p.n_kvtiles - 1);
-  const int qt_lo = ld_const(p.kvdesc, (size_t)tile * 4), qt_flo = ld_const(p.kvdesc, (size_t)tile * 4 + 1);
-  const int qt_fhi = ld_const(p.kvdesc, (size_t)tile * 4 + 2), qt_hi = ld_const(p.kvdesc, (size_t)tile * 4 + 3);
+  const int lead = min(max(ld_const(p.lpt_kv, wi.rank), 0), p.n_kvtiles - 1);
+  const int partner = min(max(ld_const(p.kv_pair, lead), 0), p.n_kvtiles - 1);
+  if (partner < lead) return;
+  const int n_parts = partner > lead ? 2 : 1;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int tkv = p.kv_hi - p.kv_lo;
-  const int key_l = tile * BK + 32 * wave + l32;    // this lane's key (local KV row)
-  const bool key_ok = key_l < tkv;
-  const int key_g = p.kv_lo + key_l;
-  const int key_end = key_ok ? doc_end(p.cu, p.n_docs, key_g) : key_g;
   const size_t kv_rstride = (size_t)p.hkv * D;
-  const bool ragged = (tile + 1) * BK > tkv;
 
-  // K and V rows of this lane's key as B operands: d = 16 s + 8 hh .. +8
-  bf16x8 kf[NKS], vf[NKS];
-  {
-    const int kl = min(key_l, tkv - 1);               // padding keys: any finite row, masked below
-    const uint16_t* kr = p.k + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * hh;
-    const uint16_t* vr = p.v + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
-      vf[s] = *reinterpret_cast<const bf16x8*>(vr + 16 * s);
-    }
-  }
+  // Per-tile state, set at the start of each part: the tile's query-block
+  // range, this lane's key, the walking direction over the query blocks.
+  int tile = lead, qt_lo = 0, qt_flo = 0, qt_fhi = 0, qt_hi = 0, dir = -1;
+  int key_l = 0, key_g = 0, key_end = 0, n_units = 0, n_steps = 0;
+  bool key_ok = false, ragged = false;
+  bf16x8 kf[NKS], vf[NKS];        // K and V rows of this lane's key as B operands: d = 16 s + 8 hh .. +8
   f32x16 dkacc[NMB], dvacc[NMB];
-#pragma unroll
-  for (int m = 0; m < NMB; ++m) { dkacc[m] = f32x16{}; dvacc[m] = f32x16{}; }
-
-  const int n_units = (qt_hi - qt_lo) * p.group;
-  if (n_units == 0) {
-    // no query row attends this tile: zero gradients
-  }
-  const int n_steps = (n_units + 1) >> 1;             // the last step may hold one dummy unit
 
   // LSE (wave 0) or Delta (wave 1) rows staged by this wave; waves 2 and 3
   // load the same words again, unused, so every wave issues the same number
   // of vector-memory instructions per step
   const float* ld_src = (wave & 1) ? p.delta : p.lse;
-  // Unit sequence: unit u is (query block qt_hi - 1 - u / G, head u % G of the
-  // group).  A wave-uniform cursor walks it in order, two units per staged
-  // step; units past the end repeat the last one (dummy units, P = 0).
+  // Unit sequence: unit u is (query block qt_hi - 1 - u / G when walking
+  // down, qt_lo + u / G when walking up; head u % G of the group).  A
+  // wave-uniform cursor walks it in order, two units per staged step; units
+  // past the end repeat the last one (dummy units, P = 0).
   struct UnitInfo {
     int l_row0, g_row0, nrows, head, masked, dummy;
   };
-  int cur_u = 0, cur_qt = qt_hi - 1, cur_hd = 0;
+  int cur_u = 0, cur_qt = 0, cur_hd = 0;
   auto next_unit = [&]() __attribute__((always_inline)) -> UnitInfo {
     UnitInfo ui;
     ui.dummy = cur_u >= n_units;
-    const int qt = ui.dummy ? qt_lo : cur_qt;
+    const int qt = ui.dummy ? (dir < 0 ? qt_lo : qt_hi - 1) : cur_qt;
     ui.head = kvh * p.group + (ui.dummy ? p.group - 1 : cur_hd);
     ui.l_row0 = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_LROW0);
     ui.g_row0 = ld_const(p.plan_kq, (size_t)qt * QP_WORDS + QP_GROW0);
@@ -168,7 +154,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     // inside the tile's FULL range every (row, key) pair is allowed
     ui.masked = (qt < qt_flo || qt >= qt_fhi || ragged || ui.nrows < BQ) ? 1 : 0;
     ++cur_u;
-    if (++cur_hd == p.group) { cur_hd = 0; --cur_qt; }
+    if (++cur_hd == p.group) { cur_hd = 0; cur_qt += dir; }
     return ui;
   };
   // lane byte offsets of the direct loads of a full unit (32 rows): row r of
@@ -432,88 +418,122 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     }
   };
 
-  if (n_units > 0) {
-    // prologue: steps 0 and 1 staged; S / dP of unit 0.  Unit 1's tiles of
-    // buffer NBUF - 1 (the operands of the "previous unit" of step 0, whose P
-    // and dS are zero) are cleared, so that 0 * garbage cannot make a NaN.
-    UnitInfo ic0, ic1, in0, in1;      // plan words of steps s and s + 1
-    issue(0, ic0, ic1);
-    issue(1, in0, in1);
+  for (int part = 0; part < n_parts; ++part) {
+    // ---- tile of this part: the leader walks its query blocks from the
+    // document end down, its partner from its diagonal up
+    tile = part ? partner : lead;
+    dir = part ? 1 : -1;
+    qt_lo = ld_const(p.kvdesc, (size_t)tile * 4);
+    qt_flo = ld_const(p.kvdesc, (size_t)tile * 4 + 1);
+    qt_fhi = ld_const(p.kvdesc, (size_t)tile * 4 + 2);
+    qt_hi = ld_const(p.kvdesc, (size_t)tile * 4 + 3);
+    key_l = tile * BK + 32 * wave + l32;              // this lane's key (local KV row)
+    key_ok = key_l < tkv;
+    key_g = p.kv_lo + key_l;
+    key_end = key_ok ? doc_end(p.cu, p.n_docs, key_g) : key_g;
+    ragged = (tile + 1) * BK > tkv;
     {
-      uint4* z = reinterpret_cast<uint4*>(&qd[NBUF - 1][2][0]);
+      const int kl = min(key_l, tkv - 1);               // padding keys: any finite row, masked below
+      const uint16_t* kr = p.k + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * hh;
+      const uint16_t* vr = p.v + (size_t)kl * kv_rstride + (size_t)kvh * D + 8 * hh;
 #pragma unroll
-      for (int i = 0; i < 2 * TB / 16 / 256; ++i) z[tid + 256 * i] = uint4{0u, 0u, 0u, 0u};
-    }
-    wait_vm(std::integral_constant<int, 0>{});
-    finish(0, ic0, ic1);
-    finish(1, in0, in1);
-    // the key's document end and the K / V operands are in registers before
-    // any later loads are in flight
-    asm volatile("" ::"v"(key_end));
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) asm volatile("" ::"a"(kf[s]), "a"(vf[s]));
-    __syncthreads();
-
-    f32x16 sa[2], da[2];
-    bf16x8 pb[2][2], dsb[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) { pb[1][t] = bf16x8{}; dsb[1][t] = bf16x8{}; }   // unit -1: adds zero
-    sdp(0, 0, sa[0], da[0]);
-    if (ic0.masked) unit_mask(ic0, sa[0]);
-    // Step s (buffer phase PH = s mod NBUF, a compile-time constant so that
-    // every LDS address is a register plus an immediate): units 2s, 2s + 1.
-    auto step = [&](int s, auto ph_c) __attribute__((always_inline)) {
-      constexpr int ph = decltype(ph_c)::value;
-      using GC = std::integral_constant<int, ph>;
-      using GP = std::integral_constant<int, (ph + NBUF - 1) % NBUF>;
-      using GN1 = std::integral_constant<int, (ph + 1) % NBUF>;
-      using J0 = std::integral_constant<int, 0>;
-      using J1 = std::integral_constant<int, 1>;
-      // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
-      UnitInfo i20, i21;
-      issue((ph + 2) % NBUF, i20, i21);
-      __builtin_amdgcn_sched_barrier(0);
-      region(GP{}, J1{}, pb[1], dsb[1], GC{}, J1{}, sa[1], da[1], GC{}, J0{}, sa[0], da[0], pb[0], dsb[0]);
-      if (ic1.masked) unit_mask(ic1, sa[1]);
-      // ---- step s + 1 staged (its loads were issued two regions ago)
-      if (s > 0) {
-        wait_vm(std::integral_constant<int, VM_PER_STEP>{});
-        finish(GN1::value, in0, in1);
+      for (int s = 0; s < NKS; ++s) {
+        kf[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
+        vf[s] = *reinterpret_cast<const bf16x8*>(vr + 16 * s);
       }
+    }
+#pragma unroll
+    for (int m = 0; m < NMB; ++m) { dkacc[m] = f32x16{}; dvacc[m] = f32x16{}; }
+    n_units = (qt_hi - qt_lo) * p.group;                // 0: no query row attends the tile (zero gradients)
+    n_steps = (n_units + 1) >> 1;                       // the last step may hold one dummy unit
+    cur_u = 0;
+    cur_qt = dir < 0 ? qt_hi - 1 : qt_lo;
+    cur_hd = 0;
+    if (part) __syncthreads();                          // the previous tile's LDS reads are done
+
+    if (n_units > 0) {
+      // prologue: steps 0 and 1 staged; S / dP of unit 0.  Unit 1's tiles of
+      // buffer NBUF - 1 (the operands of the "previous unit" of step 0, whose P
+      // and dS are zero) are cleared, so that 0 * garbage cannot make a NaN.
+      UnitInfo ic0, ic1, in0, in1;      // plan words of steps s and s + 1
+      issue(0, ic0, ic1);
+      issue(1, in0, in1);
+      {
+        uint4* z = reinterpret_cast<uint4*>(&qd[NBUF - 1][2][0]);
+#pragma unroll
+        for (int i = 0; i < 2 * TB / 16 / 256; ++i) z[tid + 256 * i] = uint4{0u, 0u, 0u, 0u};
+      }
+      wait_vm(std::integral_constant<int, 0>{});
+      finish(0, ic0, ic1);
+      finish(1, in0, in1);
+      // the key's document end and the K / V operands are in registers before
+      // any later loads are in flight
+      asm volatile("" ::"v"(key_end));
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) asm volatile("" ::"a"(kf[s]), "a"(vf[s]));
       __syncthreads();
-      // ---- region 2s + 1: dV, dK (2s) | S, dP (2s + 2) | softmax(2s + 1)
-      __builtin_amdgcn_sched_barrier(0);
-      region(GC{}, J0{}, pb[0], dsb[0], GN1{}, J0{}, sa[0], da[0], GC{}, J1{}, sa[1], da[1], pb[1], dsb[1]);
-      if (in0.masked) unit_mask(in0, sa[0]);
-      ic0 = in0; ic1 = in1; in0 = i20; in1 = i21;
-    };
-    static_assert(NBUF == 4, "one unrolled step per buffer phase");
-    for (int s = 0; s < n_steps; s += NBUF) {
-      step(s, std::integral_constant<int, 0>{});
-      if (s + 1 < n_steps) step(s + 1, std::integral_constant<int, 1>{});
-      if (s + 2 < n_steps) step(s + 2, std::integral_constant<int, 2>{});
-      if (s + 3 < n_steps) step(s + 3, std::integral_constant<int, 3>{});
-    }
-    // the last unit's dV, dK (a dummy unit adds zero)
-    dvdk((n_steps - 1) & (NBUF - 1), 1, pb[1], dsb[1]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads
-  }
 
-  // dK (scaled) and dV of this lane's key: d = 32 m + 8 j + 4 hh .. +4
-  if (key_ok) {
-    float* dkp = p.dk + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
-    float* dvp = p.dv + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
+      f32x16 sa[2], da[2];
+      bf16x8 pb[2][2], dsb[2][2];
 #pragma unroll
-    for (int m = 0; m < NMB; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = 32 * m + 8 * j;
-        *reinterpret_cast<float4*>(dkp + c) =
-            make_float4(dkacc[m][4 * j] * p.scale, dkacc[m][4 * j + 1] * p.scale, dkacc[m][4 * j + 2] * p.scale,
-                        dkacc[m][4 * j + 3] * p.scale);
-        *reinterpret_cast<float4*>(dvp + c) =
-            make_float4(dvacc[m][4 * j], dvacc[m][4 * j + 1], dvacc[m][4 * j + 2], dvacc[m][4 * j + 3]);
+      for (int t = 0; t < 2; ++t) { pb[1][t] = bf16x8{}; dsb[1][t] = bf16x8{}; }   // unit -1: adds zero
+      sdp(0, 0, sa[0], da[0]);
+      if (ic0.masked) unit_mask(ic0, sa[0]);
+      // Step s (buffer phase PH = s mod NBUF, a compile-time constant so that
+      // every LDS address is a register plus an immediate): units 2s, 2s + 1.
+      auto step = [&](int s, auto ph_c) __attribute__((always_inline)) {
+        constexpr int ph = decltype(ph_c)::value;
+        using GC = std::integral_constant<int, ph>;
+        using GP = std::integral_constant<int, (ph + NBUF - 1) % NBUF>;
+        using GN1 = std::integral_constant<int, (ph + 1) % NBUF>;
+        using J0 = std::integral_constant<int, 0>;
+        using J1 = std::integral_constant<int, 1>;
+        // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
+        UnitInfo i20, i21;
+        issue((ph + 2) % NBUF, i20, i21);
+        __builtin_amdgcn_sched_barrier(0);
+        region(GP{}, J1{}, pb[1], dsb[1], GC{}, J1{}, sa[1], da[1], GC{}, J0{}, sa[0], da[0], pb[0], dsb[0]);
+        if (ic1.masked) unit_mask(ic1, sa[1]);
+        // ---- step s + 1 staged (its loads were issued two regions ago)
+        if (s > 0) {
+          wait_vm(std::integral_constant<int, VM_PER_STEP>{});
+          finish(GN1::value, in0, in1);
+        }
+        __syncthreads();
+        // ---- region 2s + 1: dV, dK (2s) | S, dP (2s + 2) | softmax(2s + 1)
+        __builtin_amdgcn_sched_barrier(0);
+        region(GC{}, J0{}, pb[0], dsb[0], GN1{}, J0{}, sa[0], da[0], GC{}, J1{}, sa[1], da[1], pb[1], dsb[1]);
+        if (in0.masked) unit_mask(in0, sa[0]);
+        ic0 = in0; ic1 = in1; in0 = i20; in1 = i21;
+      };
+      static_assert(NBUF == 4, "one unrolled step per buffer phase");
+      for (int s = 0; s < n_steps; s += NBUF) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < n_steps) step(s + 1, std::integral_constant<int, 1>{});
+        if (s + 2 < n_steps) step(s + 2, std::integral_constant<int, 2>{});
+        if (s + 3 < n_steps) step(s + 3, std::integral_constant<int, 3>{});
       }
+      // the last unit's dV, dK (a dummy unit adds zero)
+      dvdk((n_steps - 1) & (NBUF - 1), 1, pb[1], dsb[1]);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads
+    }
+
+    // dK (scaled) and dV of this lane's key: d = 32 m + 8 j + 4 hh .. +4
+    if (key_ok) {
+      float* dkp = p.dk + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
+      float* dvp = p.dv + (size_t)key_l * kv_rstride + (size_t)kvh * D + 4 * hh;
+#pragma unroll
+      for (int m = 0; m < NMB; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 32 * m + 8 * j;
+          *reinterpret_cast<float4*>(dkp + c) =
+              make_float4(dkacc[m][4 * j] * p.scale, dkacc[m][4 * j + 1] * p.scale, dkacc[m][4 * j + 2] * p.scale,
+                          dkacc[m][4 * j + 3] * p.scale);
+          *reinterpret_cast<float4*>(dvp + c) =
+              make_float4(dvacc[m][4 * j], dvacc[m][4 * j + 1], dvacc[m][4 * j + 2], dvacc[m][4 * j + 3]);
+        }
+    }
   }
 }
 

@@ -18,6 +18,8 @@ struct SchedParams {
   int32_t* need;                   // [n_chunks][2] or null
   int32_t* key_q;                  // [n_qtiles] or null
   int32_t* key_kv;                 // [n_kvtiles] or null
+  int32_t* kv_pair;                // [n_kvtiles] KV tile paired with each tile (itself if alone) or null
+  int32_t* key_pair;               // [n_kvtiles] LPT key of the pair a tile leads (0: not a leader)
   unsigned long long* counters;    // [4] or null
   int32_t* err;                    // workspace error word
 };
@@ -58,7 +60,8 @@ struct BwdParams {
   const int32_t* cu;
   const int32_t* plan_kq; // [n_qtiles][QP_WORDS], 32-row query blocks (dK/dV kernel)
   const int32_t* kvdesc;  // [n_kvtiles][4] with bk = kBwdBK
-  const int32_t* lpt_kv;  // [n_kvtiles]
+  const int32_t* lpt_kv;  // [n_kvtiles] work items (pair leaders first, by descending work)
+  const int32_t* kv_pair; // [n_kvtiles] partner tile of each KV tile (itself if alone)
   const int32_t* plan_q;  // [n_qtiles_dq][QP_WORDS], forward-style tiles (dQ kernel)
   const int32_t* lpt_q;   // [n_qtiles_dq]
   const int32_t* err;

@@ -142,6 +142,39 @@ __global__ __launch_bounds__(256) void kvtile_kernel(SchedParams p) {
   if (p.key_kv) p.key_kv[j] = d3 - d0;
 }
 
+// Pairing of KV tiles into dK/dV work items.  Tiles with work that attend the
+// same last query tile (the tiles of one document) form a run [r0, r1) whose
+// work falls linearly along it (tile j is attended from its own position to
+// the document end); tile r0 + i is paired with tile r1 - 1 - i, so every
+// pair of a document holds about the same work, and the pairs of one document
+// that run together read the same query rows at the same time (the dK/dV
+// kernel walks the first tile from the document end down and the second one
+// from its diagonal up).  A tile without work, and the middle tile of an odd
+// run, is a work item alone.  Keys: 1 + ceil(work / 2) for a pair leader (the
+// lower tile), 0 for the other tile of a pair (it runs inside its leader's
+// work item).  One thread per run start walks the run.
+__global__ __launch_bounds__(256) void kvpair_kernel(SchedParams p) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= p.n_kvtiles) return;
+  auto last = [&](int t) { return p.kvdesc[4 * (size_t)t + 3]; };
+  auto work = [&](int t) { return p.kvdesc[4 * (size_t)t + 3] - p.kvdesc[4 * (size_t)t]; };
+  if (work(j) <= 0) {
+    p.kv_pair[j] = j;
+    p.key_pair[j] = 1;
+    return;
+  }
+  if (j > 0 && work(j - 1) > 0 && last(j - 1) == last(j)) return;   // not a run start
+  int e = j + 1;
+  while (e < p.n_kvtiles && work(e) > 0 && last(e) == last(j)) ++e;
+  for (int a = j, b = e - 1; a <= b; ++a, --b) {
+    p.kv_pair[a] = b;
+    p.kv_pair[b] = a;
+    const int w = a == b ? work(a) : work(a) + work(b);
+    p.key_pair[a] = 1 + (w + 1) / 2;
+    if (a != b) p.key_pair[b] = 0;
+  }
+}
+
 __global__ __launch_bounds__(256) void need_kernel(SchedParams p) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= p.ch.n) return;
@@ -303,6 +336,8 @@ hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv
     hipLaunchKernelGGL(qtile_kernel, dim3(ceil_div(p.n_qtiles, 256)), dim3(256), 0, stream, p);
   if (p.n_kvtiles > 0 && (p.kvdesc || p.key_kv))
     hipLaunchKernelGGL(kvtile_kernel, dim3(ceil_div(p.n_kvtiles, 256)), dim3(256), 0, stream, p);
+  if (p.kv_pair && p.kvdesc && p.n_kvtiles > 0)
+    hipLaunchKernelGGL(kvpair_kernel, dim3(ceil_div(p.n_kvtiles, 256)), dim3(256), 0, stream, p);
   if (p.need && p.ch.n > 0)
     hipLaunchKernelGGL(need_kernel, dim3(ceil_div(p.ch.n, 256)), dim3(256), 0, stream, p);
   // keys of Q tiles are KV-tile counts (<= n_kvtiles) and vice versa
@@ -314,7 +349,11 @@ hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv
       hipLaunchKernelGGL(lpt_kernel, dim3(1), dim3(1024), 0, stream, keys, n, max_key, hist, order);
   };
   if (lpt_q && p.n_qtiles > 0) lpt((const int32_t*)p.key_q, p.n_qtiles, p.n_kvtiles, lpt_q);
-  if (lpt_kv && p.n_kvtiles > 0) lpt((const int32_t*)p.key_kv, p.n_kvtiles, p.n_qtiles, lpt_kv);
+  // KV tiles (pair keys are <= 1 + n_qtiles when the tiles are paired)
+  if (lpt_kv && p.n_kvtiles > 0) {
+    if (p.kv_pair) lpt((const int32_t*)p.key_pair, p.n_kvtiles, p.n_qtiles + 1, lpt_kv);
+    else lpt((const int32_t*)p.key_kv, p.n_kvtiles, p.n_qtiles, lpt_kv);
+  }
   return hipGetLastError();
 }
 
