@@ -176,7 +176,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // lane -> row + lane / (D/8), chunk position lane % (D/8), from the tile's
   // uniform base plus a 32-bit lane offset.  Units with padded rows clamp the
   // row to the last real one (one wave-uniform branch).
-  auto issue = [&](int g, UnitInfo& u0, UnitInfo& u1) __attribute__((always_inline)) {
+  // LDS byte address of this wave's first direct-load slot in buffer 0
+  const uint32_t qd_wave =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&qd[0][0][wave * RPL * D];
+  auto issue = [&](auto g_c, UnitInfo& u0, UnitInfo& u1) __attribute__((always_inline)) {
+    constexpr int g = decltype(g_c)::value;
     u0 = next_unit();
     u1 = next_unit();
     {
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         constexpr int t = i / (WLT / 4);
-        lds_dma16_s(tb[t], loff_full[i], &qd[g][t][(wave + 4 * (i % (WLT / 4))) * RPL * D]);
+        lds_dma16_so<(uint32_t)(g * QDB + t * TB + 4 * (i % (WLT / 4)) * RPL * D * 2)>(tb[t], loff_full[i], qd_wave);
       });
     } else {
       static_for<DPW>([&](auto ic) __attribute__((always_inline)) {
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         const int r = r0 + lane / L::kChunks;
         const uint32_t off =
             (uint32_t)min(r, nrows - 1) * row_b + 16u * (uint32_t)L::chunk_at(r, lane % L::kChunks);
-        lds_dma16_s(tb[t], off, &qd[g][t][r0 * D]);
+        lds_dma16_so<(uint32_t)(g * QDB + t * TB + 4 * (i % (WLT / 4)) * RPL * D * 2)>(tb[t], off, qd_wave);
       });
     }
   };
@@ -456,8 +460,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       // buffer NBUF - 1 (the operands of the "previous unit" of step 0, whose P
       // and dS are zero) are cleared, so that 0 * garbage cannot make a NaN.
       UnitInfo ic0, ic1, in0, in1;      // plan words of steps s and s + 1
-      issue(0, ic0, ic1);
-      issue(1, in0, in1);
+      issue(std::integral_constant<int, 0>{}, ic0, ic1);
+      issue(std::integral_constant<int, 1>{}, in0, in1);
       {
         uint4* z = reinterpret_cast<uint4*>(&qd[NBUF - 1][2][0]);
 #pragma unroll
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         using J1 = std::integral_constant<int, 1>;
         // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
         UnitInfo i20, i21;
-        issue((ph + 2) % NBUF, i20, i21);
+        issue(std::integral_constant<int, (ph + 2) % NBUF>{}, i20, i21);
         __builtin_amdgcn_sched_barrier(0);
         region(GP{}, J1{}, pb[1], dsb[1], GC{}, J1{}, sa[1], da[1], GC{}, J0{}, sa[0], da[0], pb[0], dsb[0]);
         if (ic1.masked) unit_mask(ic1, sa[1]);

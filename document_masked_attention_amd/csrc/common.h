@@ -182,14 +182,16 @@ struct DenseTile {
 };
 
 // Direct 16-byte global-to-LDS load: lane l's 16 bytes land at lds_base +
-// 16 l (lds_base wave-uniform).  Completion is counted by vmcnt.  Issued as
-// inline assembly, so the compiler neither tracks the LDS write (the caller
-// waits with wait_vmem() and a barrier before any wave reads the buffer) nor
-// inserts conservative waits before unrelated LDS reads.
+// 16 l (lds_base wave-uniform, taken from M0).  Completion is counted by
+// vmcnt.  Issued as inline assembly, so the compiler neither tracks the LDS
+// write (the caller waits with wait_vmem() and a barrier before any wave reads
+// the buffer) nor inserts conservative waits before unrelated LDS reads; the
+// one wait state an LDS DMA needs after a scalar write of M0 is the s_nop.
 __device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
   const uint32_t lds_addr =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
 }
 
 // Load of a word the kernel never writes (scheduler tables), through the
@@ -203,15 +205,27 @@ __device__ __forceinline__ int32_t ld_const(const int32_t* base, size_t idx) {
 __device__ __forceinline__ void lds_dma16_s(const void* ubase, uint32_t voff, void* lds_base) {
   const uint32_t lds_addr =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ubase), "s"(lds_addr)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ubase),
+               "s"(lds_addr)
                : "memory", "m0");
+}
+
+// The same with the LDS destination given as a wave-uniform LDS byte address
+// plus a compile-time offset (one scalar add into M0): the caller keeps one
+// base register instead of one per destination.
+template <uint32_t OFF>
+__device__ __forceinline__ void lds_dma16_so(const void* ubase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ubase),
+               "s"(lds_addr), "n"(OFF)
+               : "memory", "m0", "scc");
 }
 
 // Direct 4-byte global-to-LDS load: lane l's dword lands at lds_base + 4 l.
 __device__ __forceinline__ void lds_dma4(const void* gptr, void* lds_base) {
   const uint32_t lds_addr =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
 }
 
 // Wait until this wave's global loads (including direct-to-LDS ones) are done.
