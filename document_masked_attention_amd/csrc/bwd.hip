@@ -549,10 +549,19 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   using L = SwzTile<D>;                 // K tile: row chunks and transpose reads
   constexpr int VS = D + 8;             // V tile: row chunks only (padded rows)
   constexpr int CPK = D / 8;
-  constexpr int KPP = 512 / CPK;
-  constexpr int KPASS = BK / KPP;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
+  // K and V tiles reach LDS by direct global-to-LDS loads: a tile is a run of
+  // 16-byte slots (SK / SV per row: the row's chunks plus padding slots), and
+  // direct load j fills slots 64 j .. 64 j + 63.  Lane l of load j maps slot
+  // q = 64 j + l back to (row q / S, stored position q % S): K chunk
+  // position ^ f(row) (unpadded swizzled rows), V chunk = position; padding
+  // slots load any real chunk of the row (never read).
+  constexpr int SK = L::kRowElems / 8, SV = VS / 8;
+  constexpr int WK = BK * SK / 64, WV = BK * SV / 64;       // direct loads per K / V tile
+  constexpr int DK = (WK + 7) / 8, DV = (WV + 7) / 8;       // per wave (the last may be idle)
+  static_assert(BK * SK % 64 == 0 && BK * SV % 64 == 0, "tiles are whole direct loads");
+  constexpr int KTB = BK * SK * 16, VTB = BK * SV * 16;     // bytes per K / V tile
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][L::kElems(BK)];
   __shared__ __attribute__((aligned(16))) uint16_t v_s[2][BK * VS];
 
@@ -618,28 +627,42 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   const size_t kv_rstride = (size_t)p.hkv * D;
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
-  const int kc = tid % CPK, kk0 = tid / CPK;
-  // tile base (wave-uniform) + a 32-bit byte offset per lane; padding keys
-  // clamp to the last real row (masked, any finite row will do)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)(kv_rstride * sizeof(uint16_t));
-  uint32_t loff[KPASS];
+  // lane source offsets (bytes from the tile's first row) of this wave's loads
+  uint32_t krow[DK], kchk[DK], vrow[DV], vchk[DV];
 #pragma unroll
-  for (int pp = 0; pp < KPASS; ++pp) loff[pp] = (uint32_t)(kk0 + KPP * pp) * row_bytes + 16u * kc;
-  auto load_rows = [&](const uint16_t* base, int kt, u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
-    const char* tb = reinterpret_cast<const char*>(base + (size_t)kt * BK * kv_rstride);
-    const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes + 16u * kc;
+  for (int i = 0; i < DK; ++i) {
+    const int q = (wave_u + 8 * i) * 64 + lane, r = q / SK, pos = q % SK;
+    krow[i] = (uint32_t)r * row_bytes;
+    kchk[i] = 16u * (uint32_t)(D == 128 ? (pos ^ L::f(r)) : min(pos, CPK - 1));
+  }
 #pragma unroll
-    for (int pp = 0; pp < KPASS; ++pp) reg[pp] = *reinterpret_cast<const u32x4*>(tb + min(loff[pp], lim));
-  };
-  auto store_k = [&](uint16_t* lds, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int pp = 0; pp < KPASS; ++pp)
-      *reinterpret_cast<u32x4*>(&lds[L::off(kk0 + KPP * pp, 8 * kc)]) = reg[pp];
-  };
-  auto store_v = [&](uint16_t* lds, const u32x4 (&reg)[KPASS]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int pp = 0; pp < KPASS; ++pp)
-      *reinterpret_cast<u32x4*>(&lds[(kk0 + KPP * pp) * VS + 8 * kc]) = reg[pp];
+  for (int i = 0; i < DV; ++i) {
+    const int q = (wave_u + 8 * i) * 64 + lane;
+    vrow[i] = (uint32_t)(q / SV) * row_bytes;
+    vchk[i] = 16u * (uint32_t)min(q % SV, CPK - 1);
+  }
+  const uint32_t k_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&k_s[0][0] + 1024u * wave_u;
+  const uint32_t v_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&v_s[0][0] + 1024u * wave_u;
+  // K and V tile kt into buffer BUF: uniform tile base + lane offsets; the
+  // ragged last tile clamps the row part (padding keys read the last real row:
+  // their scores are masked, any finite row will do)
+  auto issue_tile = [&](int kt, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+    const uint16_t* kb = kbase + (size_t)kt * BK * kv_rstride;
+    const uint16_t* vb = vbase + (size_t)kt * BK * kv_rstride;
+    const uint32_t lim = (uint32_t)max(tkv - 1 - kt * BK, 0) * row_bytes;
+    static_for<DK>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if (wave_u + 8 * i < WK)
+        lds_dma16_so<(uint32_t)(buf * KTB + 8 * 1024 * i)>(kb, min(krow[i], lim) + kchk[i], k_wave);
+    });
+    static_for<DV>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if (wave_u + 8 * i < WV)
+        lds_dma16_so<(uint32_t)(buf * VTB + 8 * 1024 * i)>(vb, min(vrow[i], lim) + vchk[i], v_wave);
+    });
   };
   // transpose-read source row/column for the K^T operand (keys in the S^T
   // accumulator's permuted order, see the forward kernel)
@@ -647,13 +670,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   const int kt_row = 4 * hh + (i16 >> 2), kt_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
 
   const int n = kt_hi - kt_lo;
-  if (n > 0) {
-    u32x4 kr[KPASS], vr[KPASS];
-    load_rows(kbase, kt_lo, kr);
-    load_rows(vbase, kt_lo, vr);
-    store_k(k_s[0], kr);
-    store_v(v_s[0], vr);
-  }
+  if (n > 0) issue_tile(kt_lo, std::integral_constant<int, 0>{});
+  wait_vmem();
   __syncthreads();
   // K reads: a lane byte offset inside the tile (row ln or kt_row (+ 8),
   // column block) plus a constant (buffer, 32-key block, 16-key step) in the
@@ -673,9 +691,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
     constexpr int buf = decltype(buf_c)::value;
     constexpr int KB0 = buf * L::kElems(BK) * 2;          // byte offset of this K buffer
     const int kt = kt_lo + u;
-    u32x4 kr[KPASS], vr[KPASS];
-    load_rows(kbase, min(kt + 1, kt_hi - 1), kr);    // the last tile again on the final step
-    load_rows(vbase, min(kt + 1, kt_hi - 1), vr);
+    // the next tile into the other buffer (its last reader finished before
+    // the previous barrier); in flight during this tile's math
+    if (u + 1 < n) issue_tile(kt + 1, std::integral_constant<int, buf ^ 1>{});
     const uint16_t* vs = v_s[buf];
     const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
 #pragma unroll
@@ -722,8 +740,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    store_k(k_s[buf ^ 1], kr);
-    store_v(v_s[buf ^ 1], vr);
+    wait_vmem();
     __syncthreads();
   };
   for (int u = 0; u < n; u += 2) {
