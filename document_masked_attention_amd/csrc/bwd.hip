@@ -11,7 +11,8 @@
 // Two kernels, both deterministic (no atomics), launched in this order:
 //
 // * dq_kernel, query-major, shaped like the forward.  Work item = (query tile,
-//   KV head, block of query heads), 8 waves; each wave owns 32 rows x 1 head.
+//   KV head, block of query heads), 4 waves, two workgroups per CU; each
+//   wave owns 32 rows x 1 head.
 //   It first forms Delta of its rows (unless the caller supplied it) from the
 //   dO operands it holds and the O rows, and stores it; then it walks the
 //   tile's KV range:
@@ -543,8 +544,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ dQ
 template <int D, int RB, int HB>
-__global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
-  static_assert(RB * HB == 8, "eight waves per workgroup");
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
+  constexpr int NW = RB * HB;           // waves per workgroup (two workgroups per CU)
+  static_assert(NW == 4, "four waves per workgroup");
   constexpr int BK = kDqBK;
   using L = SwzTile<D>;                 // K tile: row chunks and transpose reads
   constexpr int VS = D + 8;             // V tile: row chunks only (padded rows)
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   // slots load any real chunk of the row (never read).
   constexpr int SK = L::kRowElems / 8, SV = VS / 8;
   constexpr int WK = BK * SK / 64, WV = BK * SV / 64;       // direct loads per K / V tile
-  constexpr int DK = (WK + 7) / 8, DV = (WV + 7) / 8;       // per wave (the last may be idle)
+  constexpr int DK = (WK + NW - 1) / NW, DV = (WV + NW - 1) / NW;   // per wave (the last may be idle)
   static_assert(BK * SK % 64 == 0 && BK * SV % 64 == 0, "tiles are whole direct loads");
   constexpr int KTB = BK * SK * 16, VTB = BK * SV * 16;     // bytes per K / V tile
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][L::kElems(BK)];
@@ -633,13 +635,13 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
   uint32_t krow[DK], kchk[DK], vrow[DV], vchk[DV];
 #pragma unroll
   for (int i = 0; i < DK; ++i) {
-    const int q = (wave_u + 8 * i) * 64 + lane, r = q / SK, pos = q % SK;
+    const int q = (wave_u + NW * i) * 64 + lane, r = q / SK, pos = q % SK;
     krow[i] = (uint32_t)r * row_bytes;
     kchk[i] = 16u * (uint32_t)(D == 128 ? (pos ^ L::f(r)) : min(pos, CPK - 1));
   }
 #pragma unroll
   for (int i = 0; i < DV; ++i) {
-    const int q = (wave_u + 8 * i) * 64 + lane;
+    const int q = (wave_u + NW * i) * 64 + lane;
     vrow[i] = (uint32_t)(q / SV) * row_bytes;
     vchk[i] = 16u * (uint32_t)min(q % SV, CPK - 1);
   }
@@ -655,13 +657,13 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
     const uint32_t lim = (uint32_t)max(tkv - 1 - kt * BK, 0) * row_bytes;
     static_for<DK>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (wave_u + 8 * i < WK)
-        lds_dma16_so<(uint32_t)(buf * KTB + 8 * 1024 * i)>(kb, min(krow[i], lim) + kchk[i], k_wave);
+      if (wave_u + NW * i < WK)
+        lds_dma16_so<(uint32_t)(buf * KTB + NW * 1024 * i)>(kb, min(krow[i], lim) + kchk[i], k_wave);
     });
     static_for<DV>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (wave_u + 8 * i < WV)
-        lds_dma16_so<(uint32_t)(buf * VTB + 8 * 1024 * i)>(vb, min(vrow[i], lim) + vchk[i], v_wave);
+      if (wave_u + NW * i < WV)
+        lds_dma16_so<(uint32_t)(buf * VTB + NW * 1024 * i)>(vb, min(vrow[i], lim) + vchk[i], v_wave);
     });
   };
   // transpose-read source row/column for the K^T operand (keys in the S^T
@@ -769,10 +771,10 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(BwdParams p) {
 
 // query heads per dQ work item: as many heads of the GQA group as divide it (<= 8)
 static int dq_heads_per_item(int group) {
-  return (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  return (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
 }
 
-int dq_rows_per_tile(int group) { return 32 * (8 / dq_heads_per_item(group)); }
+int dq_rows_per_tile(int group) { return 32 * (4 / dq_heads_per_item(group)); }
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t stream) {
   // dQ first: unless the caller supplied Delta, its work items compute and
@@ -784,18 +786,16 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
   const long long nblk_q = (long long)p.n_qtiles_dq * p.hkv * a.n_hb;
   if (nblk_q > 0) {
     if (nblk_q > 0x7fffffffLL) return hipErrorInvalidValue;
-    dim3 grid((unsigned)nblk_q), block(512);
+    dim3 grid((unsigned)nblk_q), block(256);
     KernelTimer timer(KC_DQ, stream);
     if (d == 128) {
-      if (hb == 8) hipLaunchKernelGGL((dq_kernel<128, 1, 8>), grid, block, 0, stream, a);
-      else if (hb == 4) hipLaunchKernelGGL((dq_kernel<128, 2, 4>), grid, block, 0, stream, a);
-      else if (hb == 2) hipLaunchKernelGGL((dq_kernel<128, 4, 2>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((dq_kernel<128, 8, 1>), grid, block, 0, stream, a);
+      if (hb == 4) hipLaunchKernelGGL((dq_kernel<128, 1, 4>), grid, block, 0, stream, a);
+      else if (hb == 2) hipLaunchKernelGGL((dq_kernel<128, 2, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((dq_kernel<128, 4, 1>), grid, block, 0, stream, a);
     } else {
-      if (hb == 8) hipLaunchKernelGGL((dq_kernel<64, 1, 8>), grid, block, 0, stream, a);
-      else if (hb == 4) hipLaunchKernelGGL((dq_kernel<64, 2, 4>), grid, block, 0, stream, a);
-      else if (hb == 2) hipLaunchKernelGGL((dq_kernel<64, 4, 2>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((dq_kernel<64, 8, 1>), grid, block, 0, stream, a);
+      if (hb == 4) hipLaunchKernelGGL((dq_kernel<64, 1, 4>), grid, block, 0, stream, a);
+      else if (hb == 2) hipLaunchKernelGGL((dq_kernel<64, 2, 2>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((dq_kernel<64, 4, 1>), grid, block, 0, stream, a);
     }
   }
   const long long nblk_kv = (long long)p.n_kvtiles * p.hkv;
