@@ -127,15 +127,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
                         auto dp_c, auto wl_c) __attribute__((always_inline)) {
     constexpr int DP = decltype(dp_c)::value, WL = decltype(wl_c)::value;
     const uint16_t* tb = base + (size_t)kt * BK * kv_rstride;
+    // load i of every wave exists when 4 (i + 1) <= WL (no branch); only the
+    // last one may be idle on some waves
+    auto one = [&](auto ic, uint32_t off) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (4 * (i + 1) <= WL) lds_dma16_s(tb, off, lds + (wave_u + 4 * i) * 512);
+      else if (wave_u + 4 * i < WL) lds_dma16_s(tb, off, lds + (wave_u + 4 * i) * 512);
+    };
     if ((kt + 1) * BK <= tkv) {
-#pragma unroll
-      for (int i = 0; i < DP; ++i)
-        if (wave_u + 4 * i < WL) lds_dma16_s(tb, row[i] + chk[i], lds + (wave_u + 4 * i) * 512);
+      static_for<DP>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        one(ic, row[i] + chk[i]);
+      });
     } else {
       const uint32_t lim = (uint32_t)(tkv - 1 - kt * BK) * row_bytes;
-#pragma unroll
-      for (int i = 0; i < DP; ++i)
-        if (wave_u + 4 * i < WL) lds_dma16_s(tb, min(row[i], lim) + chk[i], lds + (wave_u + 4 * i) * 512);
+      static_for<DP>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        one(ic, min(row[i], lim) + chk[i]);
+      });
     }
   };
   auto issue_k = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
