@@ -657,12 +657,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     const uint32_t lim = (uint32_t)max(tkv - 1 - kt * BK, 0) * row_bytes;
     static_for<DK>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (wave_u + NW * i < WK)
+      if (NW * (i + 1) <= WK || wave_u + NW * i < WK)    // only the last load may be idle
         lds_dma16_so<(uint32_t)(buf * KTB + NW * 1024 * i)>(kb, min(krow[i], lim) + kchk[i], k_wave);
     });
     static_for<DV>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (wave_u + NW * i < WV)
+      if (NW * (i + 1) <= WV || wave_u + NW * i < WV)
         lds_dma16_so<(uint32_t)(buf * VTB + NW * 1024 * i)>(vb, min(vrow[i], lim) + vchk[i], v_wave);
     });
   };
