@@ -156,22 +156,32 @@ __global__ __launch_bounds__(256) void kvtile_kernel(SchedParams p) {
 __global__ __launch_bounds__(256) void kvpair_kernel(SchedParams p) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= p.n_kvtiles) return;
-  auto last = [&](int t) { return p.kvdesc[4 * (size_t)t + 3]; };
-  auto work = [&](int t) { return p.kvdesc[4 * (size_t)t + 3] - p.kvdesc[4 * (size_t)t]; };
-  if (work(j) <= 0) {
-    p.kv_pair[j] = j;
-    p.key_pair[j] = 1;
+  const int4* __restrict__ desc = reinterpret_cast<const int4*>(p.kvdesc);
+  int32_t* __restrict__ pair = p.kv_pair;
+  int32_t* __restrict__ key = p.key_pair;
+  const int4 dj = desc[j];
+  const int wj = dj.w - dj.x;
+  if (wj <= 0) {
+    pair[j] = j;
+    key[j] = 1;
     return;
   }
-  if (j > 0 && work(j - 1) > 0 && last(j - 1) == last(j)) return;   // not a run start
+  if (j > 0) {
+    const int4 dp = desc[j - 1];
+    if (dp.w - dp.x > 0 && dp.w == dj.w) return;                    // not a run start
+  }
   int e = j + 1;
-  while (e < p.n_kvtiles && work(e) > 0 && last(e) == last(j)) ++e;
+  for (; e < p.n_kvtiles; ++e) {
+    const int4 d = desc[e];
+    if (d.w - d.x <= 0 || d.w != dj.w) break;
+  }
   for (int a = j, b = e - 1; a <= b; ++a, --b) {
-    p.kv_pair[a] = b;
-    p.kv_pair[b] = a;
-    const int w = a == b ? work(a) : work(a) + work(b);
-    p.key_pair[a] = 1 + (w + 1) / 2;
-    if (a != b) p.key_pair[b] = 0;
+    const int4 da = desc[a], db = desc[b];
+    pair[a] = b;
+    pair[b] = a;
+    const int w = a == b ? da.w - da.x : (da.w - da.x) + (db.w - db.x);
+    key[a] = 1 + (w + 1) / 2;
+    if (a != b) key[b] = 0;
   }
 }
 
