@@ -113,10 +113,6 @@ __device__ __forceinline__ WorkItem map_work(int b, int n_ranks, int hkv, int n_
   return it;
 }
 
-__device__ __forceinline__ float wave_shfl_xor32(float x) {
-  return __shfl_xor(x, 32, 64);
-}
-
 // max / sum of x over the lane pair (l, l ^ 32) with v_permlane32_swap: the
 // swap leaves {x_l, x_(l^32)} in the two results of every lane.
 __device__ __forceinline__ float pair_max32(float x) {
@@ -181,27 +177,16 @@ struct DenseTile {
   __device__ static __forceinline__ int chunk_at(int r, int pos) { return pos ^ f(r); }
 };
 
-// Direct 16-byte global-to-LDS load: lane l's 16 bytes land at lds_base +
-// 16 l (lds_base wave-uniform, taken from M0).  Completion is counted by
-// vmcnt.  Issued as inline assembly, so the compiler neither tracks the LDS
-// write (the caller waits with wait_vmem() and a barrier before any wave reads
-// the buffer) nor inserts conservative waits before unrelated LDS reads; the
-// one wait state an LDS DMA needs after a scalar write of M0 is the s_nop.
-__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
-  const uint32_t lds_addr =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
-               : "memory", "m0");
-}
+// Direct 16-byte global-to-LDS loads (inline assembly): lane l's 16 bytes
+// land at M0 + 16 l, the LDS destination being wave-uniform.  Completion is
+// counted by vmcnt.  The compiler neither tracks the LDS write (the caller
+// waits with wait_vmem() or a counted vmcnt and a barrier before any wave
+// reads the buffer) nor inserts conservative waits before unrelated LDS
+// reads; the one wait state an LDS DMA needs after a scalar write of M0 is
+// the s_nop.
 
-// Load of a word the kernel never writes (scheduler tables), through the
-// constant address space so that a wave-uniform index becomes a scalar load.
-__device__ __forceinline__ int32_t ld_const(const int32_t* base, size_t idx) {
-  return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
-}
-
-// The same 16-byte load from a wave-uniform base (SGPRs) plus a 32-bit lane
-// byte offset: no per-lane 64-bit address arithmetic.
+// From a wave-uniform base (SGPRs) plus a 32-bit lane byte offset: no
+// per-lane 64-bit address arithmetic.
 __device__ __forceinline__ void lds_dma16_s(const void* ubase, uint32_t voff, void* lds_base) {
   const uint32_t lds_addr =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
@@ -228,23 +213,14 @@ __device__ __forceinline__ void lds_dma4(const void* gptr, void* lds_base) {
                : "memory", "m0");
 }
 
+// Load of a word the kernel never writes (scheduler tables), through the
+// constant address space so that a wave-uniform index becomes a scalar load.
+__device__ __forceinline__ int32_t ld_const(const int32_t* base, size_t idx) {
+  return ((const __attribute__((address_space(4))) int32_t*)(base))[idx];
+}
+
 // Wait until this wave's global loads (including direct-to-LDS ones) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
-
-// Scheduling hint for a block of G groups, each `reads` LDS reads feeding
-// `mfmas` MFMAs: the reads of the first two groups are issued first, then
-// every group's MFMAs are followed by the reads of the group two ahead, so
-// LDS latency overlaps matrix work.  Only reorders; no effect on results.
-template <int G, int READS, int MFMAS>
-__device__ __forceinline__ void sched_reads_ahead() {
-  constexpr int kMfma = 0x008, kDsRead = 0x100;
-  __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * READS, 0);
-  static_for<G>([&](auto ic) __attribute__((always_inline)) {
-    constexpr int i = decltype(ic)::value;
-    __builtin_amdgcn_sched_group_barrier(kMfma, MFMAS, 0);
-    if (i + 2 < G) __builtin_amdgcn_sched_group_barrier(kDsRead, READS, 0);
-  });
-}
 
 // Two transpose reads assembled into one 8 x bf16 MFMA operand.
 __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p0, const uint16_t* p1) {
