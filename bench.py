@@ -259,7 +259,8 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_merge:
-        result["components"]["merge"] = bench_merge(api, torch, dev, upload, args.steps)
+        result["components"]["merge"], result["components"]["cp_rank_forward"] = bench_merge(
+            api, torch, dev, upload, args.steps)
     if args.copy_calibration:
         # a streaming kernel of known size for scaling HBM byte counters: the
         # library's f32 -> bf16 conversion reads 1 GiB and writes 512 MiB
@@ -287,6 +288,7 @@ def bench_merge(api, torch, dev, upload, steps):
     need = api.schedule(cu, w.chunks, w.kv_lo, w.kv_hi, 8192, 8192)["need"].cpu().numpy()
     blk = w.kv_block
     jobs = []
+    fwd_calls = []
     row0 = 0
     total_bytes = 0.0
     dense_bytes = 0.0
@@ -304,8 +306,42 @@ def bench_merge(api, torch, dev, upload, steps):
         total_bytes += p_c * n * w.hq * 4 + finite * 2 * w.d + n * w.hq * (2 * w.d + 4)
         dense_bytes += p_c * n * w.hq * (4 + 2 * w.d) + n * w.hq * (2 * w.d + 4)
         jobs.append((po, pl, oo, lo))
+        fwd_calls.append((row0, g, n, blocks, po, pl))
         row0 += n
     torch.cuda.synchronize()
+
+    # the rank's forward as the pages' ring schedule runs it: one call per
+    # (chunk, KV block), partials merged afterwards (timed below on its own)
+    def fwd_all():
+        for r0, g, n, blocks, po, pl in fwd_calls:
+            for i, b in enumerate(blocks):
+                api.attn_fwd(q[r0:r0 + n], k[blk * b:blk * (b + 1)], v[blk * b:blk * (b + 1)], cu, [(g, n)],
+                             blk * b, blk * (b + 1), w.scale, out=po[i], lse=pl[i])
+
+    reps = max(steps, 5)
+    fwd_all()
+    torch.cuda.synchronize()
+    api.timing_enable(True)
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(reps):
+        fwd_all()
+    f1.record()
+    torch.cuda.synchronize()
+    t_fwd, n_fwd = api.timing_read(api.KERNEL_FWD)
+    t_sch, _ = api.timing_read(api.KERNEL_SCHEDULE)
+    api.timing_enable(False)
+    wall_ms = f0.elapsed_time(f1) / reps
+    kern_ms = (t_fwd + t_sch) / reps
+    pairs = int(api.schedule(cu, w.chunks, w.kv_lo, w.kv_hi, 128, 64)["counters"][3].item())
+    flop = 4.0 * w.d * w.hq * pairs
+    cp_fwd = {"workload": w.name, "calls_per_pass": n_fwd // reps, "pairs_per_head": pairs,
+              "useful_tflop": round(flop / 1e12, 3), "kernel_ms": round(kern_ms, 4), "wall_ms": round(wall_ms, 4),
+              "tflops_kernel": round(flop / (kern_ms * 1e-3) / 1e12, 2),
+              "frac_of_peak": round(flop / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+              "note": "sum of the per-(chunk, 8192-key block) forward calls' scheduler and kernel time; "
+                      "wall_ms includes host launch overhead"}
 
     def merge_all():
         for po, pl, oo, lo in jobs:
@@ -323,9 +359,10 @@ def bench_merge(api, torch, dev, upload, steps):
     ms = e0.elapsed_time(e1) / max(steps, 10)
     gbs = total_bytes / (ms * 1e-3) / 1e9
     parts = [j[0].shape[0] for j in jobs]
-    return {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
-            "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "bound": "hbm"}
+    merge = {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
+             "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+             "bound": "hbm"}
+    return merge, cp_fwd
 
 
 if __name__ == "__main__":
