@@ -79,7 +79,9 @@ __device__ __forceinline__ void mfma_v_settle() { asm volatile("s_nop 7\n\ts_nop
 // Units are software-pipelined: region u runs the softmax of unit u on the
 // vector ALU while the matrix cores run dV / dK of unit u - 1 and S / dP of
 // unit u + 1.  Two units form a staging step; steps go through a ring of four
-// LDS buffers filled by direct global-to-LDS loads two steps ahead.
+// LDS buffers filled by direct global-to-LDS loads: step s + 3 is issued in
+// the middle of step s, as soon as the barrier there frees the buffer of
+// step s - 1.
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
@@ -168,8 +170,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     const int r = (wave + 4 * (i % (WLT / 4))) * RPL + lane / L::kChunks;
     loff_full[i] = (uint32_t)r * row_b + 16u * (uint32_t)L::chunk_at(r, lane % L::kChunks);
   }
-  // Loads of the next step (its two units come back in u0 / u1) into stage
-  // dst, all direct global-to-LDS loads (no register is written
+  // Loads of the next step to stage (its two units come back in u0 / u1)
+  // into buffer g, all direct global-to-LDS loads (no register is written
   // asynchronously): per wave first one dword per lane into raw[tid] (threads
   // 0..127: LSE then Delta of unit (tid / 32) % 2, row tid % 32 clamped to a
   // real row), then DPW 16-byte loads: load i covers tile t = i / (WLT / 4)
@@ -457,18 +459,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     if (part) __syncthreads();                          // the previous tile's LDS reads are done
 
     if (n_units > 0) {
-      // prologue: steps 0 and 1 staged; S / dP of unit 0.  Unit 1's tiles of
-      // buffer NBUF - 1 (the operands of the "previous unit" of step 0, whose P
-      // and dS are zero) are cleared, so that 0 * garbage cannot make a NaN.
-      UnitInfo ic0, ic1, in0, in1;      // plan words of steps s and s + 1
+      // prologue: steps 0 and 1 staged, step 2 in flight; S / dP of unit 0.
+      // Unit 1's tiles of buffer NBUF - 1 (the operands of the "previous
+      // unit" of step 0, whose P and dS are zero) are cleared, so that
+      // 0 * garbage cannot make a NaN.
+      UnitInfo ic0, ic1, in0, in1, i20, i21;   // plan words of steps s, s + 1, s + 2
       issue(std::integral_constant<int, 0>{}, ic0, ic1);
       issue(std::integral_constant<int, 1>{}, in0, in1);
+      issue(std::integral_constant<int, 2>{}, i20, i21);
       {
         uint4* z = reinterpret_cast<uint4*>(&qd[NBUF - 1][2][0]);
 #pragma unroll
         for (int i = 0; i < 2 * TB / 16 / 256; ++i) z[tid + 256 * i] = uint4{0u, 0u, 0u, 0u};
       }
-      wait_vm(std::integral_constant<int, 0>{});
+      wait_vm(std::integral_constant<int, VM_PER_STEP>{});
       finish(0, ic0, ic1);
       finish(1, in0, in1);
       // the key's document end and the K / V operands are in registers before
@@ -494,22 +498,25 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         using J0 = std::integral_constant<int, 0>;
         using J1 = std::integral_constant<int, 1>;
         // ---- region 2s: dV, dK (2s - 1) | S, dP (2s + 1) | softmax(2s)
-        UnitInfo i20, i21;
-        issue(std::integral_constant<int, (ph + 2) % NBUF>{}, i20, i21);
         __builtin_amdgcn_sched_barrier(0);
         region(GP{}, J1{}, pb[1], dsb[1], GC{}, J1{}, sa[1], da[1], GC{}, J0{}, sa[0], da[0], pb[0], dsb[0]);
         if (ic1.masked) unit_mask(ic1, sa[1]);
-        // ---- step s + 1 staged (its loads were issued two regions ago)
+        // ---- step s + 1 staged (its loads were issued four regions ago;
+        // step s + 2's may still be in flight)
         if (s > 0) {
           wait_vm(std::integral_constant<int, VM_PER_STEP>{});
           finish(GN1::value, in0, in1);
         }
         __syncthreads();
+        // ---- step s + 3 into the buffer of step s - 1, whose last reader
+        // (region 2s, the previous unit's dV / dK) is behind the barrier
+        UnitInfo i30, i31;
+        issue(std::integral_constant<int, (ph + 3) % NBUF>{}, i30, i31);
         // ---- region 2s + 1: dV, dK (2s) | S, dP (2s + 2) | softmax(2s + 1)
         __builtin_amdgcn_sched_barrier(0);
         region(GC{}, J0{}, pb[0], dsb[0], GN1{}, J0{}, sa[0], da[0], GC{}, J1{}, sa[1], da[1], pb[1], dsb[1]);
         if (in0.masked) unit_mask(in0, sa[0]);
-        ic0 = in0; ic1 = in1; in0 = i20; in1 = i21;
+        ic0 = in0; ic1 = in1; in0 = i20; in1 = i21; i20 = i30; i21 = i31;
       };
       static_assert(NBUF == 4, "one unrolled step per buffer phase");
       for (int s = 0; s < n_steps; s += NBUF) {
