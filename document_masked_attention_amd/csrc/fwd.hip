@@ -159,15 +159,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   // S^T = K Q^T for the two 32-key blocks of the tile held in K buffer kb_
   auto compute_s = [&](const uint16_t* kl, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+    // the two 32-key blocks alternate, so consecutive MFMAs are independent
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int s = 0; s < NKS; ++s)
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&kl[(32 * kb + ln) * KSTR + 16 * s + 8 * hh]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
       }
-    }
   };
 
   // Pipeline over the n tiles (index u = kt - kt_lo): K tile u lives in
