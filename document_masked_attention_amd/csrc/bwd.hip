@@ -591,47 +591,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const bool row_ok = qr < nrows;
   const int gi = g_row0 + qr;
   const size_t o_off = ((size_t)(l_row0 + qr) * p.hq + head) * D;
-  int a_lo = 0x40000000, a_w = 0;
-  float lse2 = INFINITY, dlt = 0.f;
-  if (row_ok) {
-    const int lo = max(doc_start(p.cu, p.n_docs, gi), p.kv_lo), hi = min(gi, p.kv_hi - 1);
-    if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
-    const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr];
-    lse2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
-    if (p.delta_ready) dlt = p.delta[(size_t)head * p.tq + l_row0 + qr];
-  }
-  bf16x8 qf[NKS], dof[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    qf[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh) : bf16x8{};
-    dof[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.d_o + o_off + 16 * s + 8 * hh) : bf16x8{};
-  }
-  // Delta = rowsum(dO * O) for this row and head, unless the caller supplied
-  // it: this lane's half of the row (d = 16 s + 8 hh .. +8) from the dO
-  // operands already in registers, then the lane pair's sum.  Each (row,
-  // head) belongs to exactly one dQ work item, which stores it for the dK/dV
-  // kernel that runs next.
-  if (!p.delta_ready) {
-    float part = 0.f;
-    if (row_ok) {
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + o_off + 16 * s + 8 * hh);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)ov[e], (float)dof[s][e], part);
-      }
-    }
-    dlt = pair_sum32(part);
-    if (row_ok && hh == 0) p.delta[(size_t)head * p.tq + l_row0 + qr] = dlt;
-  }
-  f32x16 dqacc[NDB];
-#pragma unroll
-  for (int b = 0; b < NDB; ++b) dqacc[b] = f32x16{};
-  // -Delta of this lane's row in every accumulator entry: the initial dP^T
-  f32x16 ndlt;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) ndlt[r] = -dlt;
-
   const int tkv = p.kv_hi - p.kv_lo;
   const size_t kv_rstride = (size_t)p.hkv * D;
   const uint16_t* kbase = p.k + (size_t)kvh * D;
@@ -673,13 +632,55 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         lds_dma16_so<(uint32_t)(buf * VTB + NW * 1024 * i)>(vb, min(vrow[i], lim) + vchk[i], v_wave);
     });
   };
+  // the first K / V tile is in flight while the row operands load
+  const int n = kt_hi - kt_lo;
+  if (n > 0) issue_tile(kt_lo, std::integral_constant<int, 0>{});
+  int a_lo = 0x40000000, a_w = 0;
+  float lse2 = INFINITY, dlt = 0.f;
+  if (row_ok) {
+    const int lo = max(doc_start(p.cu, p.n_docs, gi), p.kv_lo), hi = min(gi, p.kv_hi - 1);
+    if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
+    const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr];
+    lse2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
+    if (p.delta_ready) dlt = p.delta[(size_t)head * p.tq + l_row0 + qr];
+  }
+  bf16x8 qf[NKS], dof[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    qf[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh) : bf16x8{};
+    dof[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.d_o + o_off + 16 * s + 8 * hh) : bf16x8{};
+  }
+  // Delta = rowsum(dO * O) for this row and head, unless the caller supplied
+  // it: this lane's half of the row (d = 16 s + 8 hh .. +8) from the dO
+  // operands already in registers, then the lane pair's sum.  Each (row,
+  // head) belongs to exactly one dQ work item, which stores it for the dK/dV
+  // kernel that runs next.
+  if (!p.delta_ready) {
+    float part = 0.f;
+    if (row_ok) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + o_off + 16 * s + 8 * hh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)ov[e], (float)dof[s][e], part);
+      }
+    }
+    dlt = pair_sum32(part);
+    if (row_ok && hh == 0) p.delta[(size_t)head * p.tq + l_row0 + qr] = dlt;
+  }
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) dqacc[b] = f32x16{};
+  // -Delta of this lane's row in every accumulator entry: the initial dP^T
+  f32x16 ndlt;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndlt[r] = -dlt;
+
   // transpose-read source row/column for the K^T operand (keys in the S^T
   // accumulator's permuted order, see the forward kernel)
   const int i16 = lane & 15;
   const int kt_row = 4 * hh + (i16 >> 2), kt_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
 
-  const int n = kt_hi - kt_lo;
-  if (n > 0) issue_tile(kt_lo, std::integral_constant<int, 0>{});
   wait_vmem();
   __syncthreads();
   // K reads: a lane byte offset inside the tile (row ln or kt_row (+ 8),

@@ -78,13 +78,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
   }
 
-  // Q operand of this lane: row qr, d = 16 s + 8 hh .. +8, for every k-step s.
-  bf16x8 qf[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    if (row_ok) qf[s] = *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh);
-    else qf[s] = bf16x8{};
-  }
+  bf16x8 qf[NKS];            // Q operand of this lane: row qr, d = 16 s + 8 hh .. +8, k-step s
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -180,6 +174,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     issue_k(kt_lo, k_lds[0]);
     issue_v(kt_lo, v_lds[0]);
     issue_k(min(kt_lo + 1, kt_hi - 1), k_lds[1]);
+  }
+  // the first tiles are in flight while the Q operands load
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    if (row_ok) qf[s] = *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh);
+    else qf[s] = bf16x8{};
+  }
+  if (n > 0) {
     wait_vmem();
     __syncthreads();
     compute_s(k_lds[0], s_cur);
