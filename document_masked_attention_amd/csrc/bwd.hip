@@ -18,9 +18,10 @@
 //   tile's KV range:
 //     S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T
 //   (v_mfma_f32_32x32x16_bf16; K^T through transpose reads).
-// * dkdv_kernel, key-major.  Work item = (KV tile of 128 keys, KV head);
-//   4 waves x 32 keys (one wave per SIMD), each lane keeping one key's K and
-//   V rows (MFMA B operands) and its dK, dV accumulators in registers.  It
+// * dkdv_kernel, key-major.  Work item = (one or two KV tiles of 128 keys
+//   of a document, paired by the scheduler, KV head); 4 waves x 32 keys (one
+//   wave per SIMD), each lane keeping one key's K and V rows (MFMA B
+//   operands) and its dK, dV accumulators in registers.  For each tile it
 //   walks every (32-row query block, query head of the group) that attends
 //   the tile -- the scheduler's per-KV-tile range -- with the Q and dO rows
 //   staged in LDS:
@@ -61,8 +62,9 @@ __device__ __forceinline__ void mfma_v_acc(f32x16& c, const bf16x8& a, const bf1
 __device__ __forceinline__ void mfma_v_settle() { asm volatile("s_nop 7\n\ts_nop 3"); }
 
 // ------------------------------------------------------------------ dK, dV
-// Work item = (KV tile of 128 keys, KV head); four waves of 32 keys, one
-// wave per SIMD.  Each lane keeps one key: its K and V rows are the MFMA B
+// Work item = (pair of KV tiles of 128 keys, KV head), the tiles processed
+// one after the other; four waves of 32 keys, one wave per SIMD.  Each lane
+// keeps one key: its K and V rows are the MFMA B
 // operands of S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16), whose
 // output tiles hold 16 query rows {8 j + 4 h + r} of that key per lane.  In
 // that register order P and dS are directly the B operands of dV^T += dO^T P
@@ -73,9 +75,10 @@ __device__ __forceinline__ void mfma_v_settle() { asm volatile("s_nop 7\n\ts_nop
 // the scores of disallowed pairs set to -inf (only units outside the tile's
 // FULL range, in a branch between pipeline regions).
 //
-// The work is a sequence of units (32-row query block, query head), query
-// blocks from the last one down: the tiles of one document running at the
-// same time then read the same Q / dO rows together, which keeps them in L2.
+// Per tile the work is a sequence of units (32-row query block, query head):
+// the first tile of a pair walks its query blocks from the last one down, the
+// second from its first one up, so that the work items of one document
+// running at the same time read the same Q / dO rows together (L2 reuse).
 // Units are software-pipelined: region u runs the softmax of unit u on the
 // vector ALU while the matrix cores run dV / dK of unit u - 1 and S / dP of
 // unit u + 1.  Two units form a staging step; steps go through a ring of four
