@@ -711,8 +711,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // MFMA phases at raised wave priority (the other wave of the SIMD fills
-      // the gaps with its vector work)
+      // the S / dP MFMAs at raised wave priority (the other wave of the SIMD
+      // fills the gaps with its vector work)
       __builtin_amdgcn_s_setprio(1);
       f32x16 sacc = f32x16{}, dpacc = ndlt;          // dP^T starts from -Delta: dS^T = P^T dP^T
 #pragma unroll
@@ -738,7 +738,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse2));
         ds[r] = pr * dpacc[r];
       }
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const bf16x8 dsb = cvt8(ds[8 * k2], ds[8 * k2 + 1], ds[8 * k2 + 2], ds[8 * k2 + 3], ds[8 * k2 + 4],
@@ -752,7 +751,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         }
       }
     }
-    __builtin_amdgcn_s_setprio(0);
     wait_vmem();
     __syncthreads();
   };
