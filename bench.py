@@ -359,6 +359,27 @@ def bench_merge(api, torch, dev, upload, steps):
     ms = e0.elapsed_time(e1) / max(steps, 10)
     gbs = total_bytes / (ms * 1e-3) / 1e9
     parts = [j[0].shape[0] for j in jobs]
+    # the same rows in one call over the whole KV range (no partials, no merge)
+    o1 = torch.empty((w.tq, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    l1 = torch.empty((w.hq, w.tq), dtype=torch.float32, device=dev)
+
+    def fwd_one():
+        api.attn_fwd(q, k, v, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale, out=o1, lse=l1)
+
+    fwd_one()
+    torch.cuda.synchronize()
+    api.timing_enable(True)
+    for _ in range(reps):
+        fwd_one()
+    torch.cuda.synchronize()
+    t1, _ = api.timing_read(api.KERNEL_FWD)
+    t1s, _ = api.timing_read(api.KERNEL_SCHEDULE)
+    api.timing_enable(False)
+    one_ms = (t1 + t1s) / reps
+    cp_fwd.update({"per_block_plus_merge_ms": round(kern_ms + ms, 4),
+                   "single_call_kernel_ms": round(one_ms, 4),
+                   "single_call_tflops": round(flop / (one_ms * 1e-3) / 1e12, 2),
+                   "single_call_frac_of_peak": round(flop / (one_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
     merge = {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
              "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
              "bound": "hbm"}
