@@ -118,11 +118,18 @@ def main():
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the f32->bf16 conversion over 1 GiB (reference for HBM byte counters)")
+    ap.add_argument("--study", choices=["sharding"],
+                    help="instead of the step benchmark, time every CP rank's forward under per-sequence and "
+                         "per-document 2 x CP sharding (1 x 131072, 16 x 8192 and bimodal documents)")
+    ap.add_argument("--cp", type=int, default=8, help="CP size of the sharding study")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of it",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.study == "sharding":
+        study_sharding(args.cp, max(args.steps, 3))
+        return
 
     import torch
     import oracle  # noqa: F401  (imported only for the cpu_baseline leg)
@@ -384,6 +391,120 @@ def bench_merge(api, torch, dev, upload, steps):
              "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
              "bound": "hbm"}
     return merge, cp_fwd
+
+
+def study_sharding(cp: int, reps: int):
+    """Kernel-efficiency study of 2 x CP sharding on one GPU (the single-GPU
+    analogue of FlashCP Figure 3).  For every rank r of a CP group of size cp,
+    the rank's forward is run three ways over the all-gathered KV range:
+
+      per_sequence        chunks r and 2cp-1-r of the packed sequence, one call;
+      per_doc             pieces r and 2cp-1-r of every document, one call;
+      per_doc_blockwise   the same rows computed block by block, one call per
+                          contiguous KV block of T/cp keys that the rows need,
+                          then the partials merged (ring-style execution).
+
+    Time per rank = the library's event timer summed over scheduler, forward
+    and merge kernels; a CP step is as slow as its slowest rank."""
+    import torch
+    from document_masked_attention_amd import api
+    from document_masked_attention_amd.workloads import (FIG3_PATTERNS, fig3_lengths, fig3_workload, draw_tensor,
+                                                         cu_from_lengths)
+    api.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hq, hkv, d, seed = 32, 8, 128, 5
+    out = {"study": "2xCP sharding, one rank's forward over the all-gathered KV", "cp": cp, "q_heads": hq,
+           "kv_heads": hkv, "head_dim": d, "reps": reps, "time": "scheduler + forward (+ merge) kernel ms",
+           "patterns": {}}
+
+    def dev_bits(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def lib_ms(classes):
+        return sum(api.timing_read(c)[0] for c in classes) / reps
+
+    for pattern in FIG3_PATTERNS:
+        lengths = fig3_lengths(pattern, seed)
+        total = int(sum(lengths))
+        log(f"[study] {pattern}: {len(lengths)} documents, generating inputs")
+        qf = dev_bits(draw_tensor(seed, "q", total, hq, d))
+        kf = dev_bits(draw_tensor(seed, "k", total, hkv, d))
+        vf = dev_bits(draw_tensor(seed, "v", total, hkv, d))
+        cu = torch.as_tensor(cu_from_lengths(lengths), dtype=torch.int32, device=dev)
+        blk = total // cp
+        res = {s: {"per_rank_ms": [], "per_rank_wall_ms": [], "per_rank_pairs": [], "per_rank_chunks": []}
+               for s in ("per_sequence", "per_doc", "per_doc_blockwise")}
+        scale = 1.0 / np.sqrt(d)
+        for r in range(cp):
+            for sharding in ("per_sequence", "per_doc"):
+                w = fig3_workload(pattern, sharding, cp, r, hq, hkv, d, seed)
+                pos = torch.as_tensor(w.local_positions(), device=dev)
+                q = qf.index_select(0, pos)
+                o = torch.empty((w.tq, hq, d), dtype=torch.bfloat16, device=dev)
+                lse = torch.empty((hq, w.tq), dtype=torch.float32, device=dev)
+                ws = torch.empty(api.workspace_size(api.OP_FWD, len(lengths), w.chunks, 0, total, hq, hkv, d),
+                                 dtype=torch.uint8, device=dev)
+                sched = api.schedule(cu, w.chunks, 0, total, 128, 64)
+                pairs = int(sched["counters"][3].item())
+                need = sched["need"].cpu().numpy()
+                variants = [(sharding, None)]
+                if sharding == "per_doc":
+                    lo = int(need[:, 0][need[:, 1] > need[:, 0]].min())
+                    hi = int(need[:, 1].max())
+                    blocks = [b for b in range(cp) if b * blk < hi and (b + 1) * blk > lo]
+                    po = torch.empty((len(blocks), w.tq, hq, d), dtype=torch.bfloat16, device=dev)
+                    pl = torch.empty((len(blocks), hq, w.tq), dtype=torch.float32, device=dev)
+                    variants.append(("per_doc_blockwise", blocks))
+
+                for name, blocks in variants:
+                    if blocks is None:
+                        def run():
+                            api.attn_fwd(q, kf, vf, cu, w.chunks, 0, total, scale, out=o, lse=lse, workspace=ws)
+                    else:
+                        def run():
+                            for i, b in enumerate(blocks):
+                                api.attn_fwd(q, kf[b * blk:(b + 1) * blk], vf[b * blk:(b + 1) * blk], cu, w.chunks,
+                                             b * blk, (b + 1) * blk, scale, out=po[i], lse=pl[i])
+                            api.lse_merge(po, pl, o_out=o, lse_out=lse)
+                    run()
+                    torch.cuda.synchronize()
+                    api.timing_enable(True)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(reps):
+                        run()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms = lib_ms((api.KERNEL_SCHEDULE, api.KERNEL_FWD, api.KERNEL_MERGE))
+                    api.timing_enable(False)
+                    rr = res[name]
+                    rr["per_rank_ms"].append(round(ms, 4))
+                    rr["per_rank_wall_ms"].append(round(e0.elapsed_time(e1) / reps, 4))
+                    rr["per_rank_pairs"].append(pairs)
+                    rr["per_rank_chunks"].append(len(w.chunks))
+                    if blocks is not None:
+                        rr.setdefault("kv_blocks_per_rank", []).append(len(blocks))
+                del q, o, lse, ws
+                if sharding == "per_doc":
+                    del po, pl
+            log(f"[study] {pattern} rank {r}: " + ", ".join(f"{k} {v['per_rank_ms'][-1]:.3f} ms"
+                                                            for k, v in res.items()))
+        base = max(res["per_sequence"]["per_rank_ms"])
+        for name, rr in res.items():
+            ms = np.array(rr["per_rank_ms"])
+            pr = np.array(rr["per_rank_pairs"], dtype=np.float64)
+            flop = 4.0 * d * hq * pr
+            rr.update({"max_ms": round(float(ms.max()), 4), "mean_ms": round(float(ms.mean()), 4),
+                       "normalized_latency": round(float(ms.max()) / base, 4),
+                       "pair_imbalance": round(float(pr.max() / pr.mean()), 4),
+                       "mean_rank_tflops": round(float((flop / (ms * 1e-3)).mean() / 1e12), 2),
+                       "mean_rank_frac_of_peak": round(float((flop / (ms * 1e-3)).mean() / 1e12 / PEAK_BF16_TFLOPS), 4)})
+        out["patterns"][pattern] = {"documents": len(lengths), **res}
+        del qf, kf, vf
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -229,6 +229,73 @@ def custom_workload(seed: int, lengths, hq: int, hkv: int, d: int, chunks=None, 
                     total if kv_hi is None else kv_hi, backward)
 
 
+def sequence_zigzag_chunks(total: int, cp: int, rank: int) -> list:
+    """Per-sequence 2 x CP sharding: the packed sequence cut into 2*cp equal
+    chunks, rank r holding chunks r and 2*cp - 1 - r (FlashCP section 2.3, the
+    sharding that Llama3 CP and Ring-Attn (Zigzag) start from).  ``total`` must
+    be a multiple of 2*cp."""
+    if total % (2 * cp):
+        raise ValueError("total must be a multiple of 2 * cp")
+    c = total // (2 * cp)
+    return [(rank * c, c), ((2 * cp - 1 - rank) * c, c)]
+
+
+def doc_piece_bounds(length: int, cp: int) -> list:
+    """Boundaries of the 2*cp pieces of one document: piece i covers local rows
+    [floor(i*L/(2cp)), floor((i+1)*L/(2cp))), so pieces differ by at most one
+    row and a document shorter than 2*cp leaves some pieces empty."""
+    n = 2 * cp
+    return [(i * length) // n for i in range(n + 1)]
+
+
+def per_doc_chunks(lengths, cp: int, rank: int) -> list:
+    """Per-document 2 x CP sharding (Per-Doc CP and Ring-Attn (Zigzag) varlen,
+    FlashCP section 2.3): every document cut into 2*cp pieces, rank r holding
+    pieces r and 2*cp - 1 - r of each.  Returned in ascending position order
+    (document by document), empty pieces dropped; adjacent pieces stay separate
+    chunks."""
+    out = []
+    start = 0
+    for length in map(int, lengths):
+        b = doc_piece_bounds(length, cp)
+        for i in (rank, 2 * cp - 1 - rank):
+            if b[i + 1] > b[i]:
+                out.append((start + b[i], b[i + 1] - b[i]))
+        start += length
+    return out
+
+
+FIG3_PATTERNS = ("1x131072", "16x8192", "bimodal131072")
+
+
+def fig3_lengths(pattern: str, seed: int = 5) -> list:
+    """Document lengths of the kernel-efficiency study (FlashCP Figure 3: one
+    128K document vs sixteen 8K documents), plus the bimodal 131072-token mix."""
+    if pattern == "1x131072":
+        return [131072]
+    if pattern == "16x8192":
+        return [8192] * 16
+    if pattern == "bimodal131072":
+        return bimodal_docs(seed, 131072)
+    raise ValueError(f"unknown pattern {pattern}")
+
+
+def fig3_workload(pattern: str, sharding: str, cp: int, rank: int, hq: int = 32, hkv: int = 8, d: int = 128,
+                  seed: int = 5) -> Workload:
+    """One CP rank's forward under per-sequence or per-document 2 x CP sharding,
+    attending the whole (all-gathered) KV range."""
+    lengths = fig3_lengths(pattern, seed)
+    total = int(sum(lengths))
+    if sharding == "per_sequence":
+        chunks = sequence_zigzag_chunks(total, cp, rank)
+    elif sharding == "per_doc":
+        chunks = per_doc_chunks(lengths, cp, rank)
+    else:
+        raise ValueError(f"unknown sharding {sharding}")
+    return Workload(f"{sharding}_cp{cp}_rank{rank}_{pattern}_h{hq}x{hkv}_d{d}", seed, total, lengths, hq, hkv, d,
+                    chunks, 0, total, meta={"cp": cp, "rank": rank, "pattern": pattern, "sharding": sharding})
+
+
 def random_lengths(rng: np.random.Generator, total: int, max_len: int, p_one: float = 0.15) -> list[int]:
     """Random document split of ``total`` tokens, with some length-1 documents."""
     out = []
