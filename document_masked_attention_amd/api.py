@@ -22,8 +22,8 @@ ACCUMULATE_DQ = 1
 DELTA_READY = 2
 MAX_CHUNKS = 256
 (KERNEL_SCHEDULE, KERNEL_FWD, KERNEL_DELTA, KERNEL_DKDV, KERNEL_DQ, KERNEL_MERGE,
- KERNEL_CONVERT) = range(7)
-N_KERNEL_CLASSES = 7
+ KERNEL_CONVERT, KERNEL_COPY) = range(8)
+N_KERNEL_CLASSES = 8
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -34,6 +34,10 @@ _f32 = ctypes.c_float
 
 class Chunk(ctypes.Structure):
     _fields_ = [("g_start", ctypes.c_int32), ("len", ctypes.c_int32)]
+
+
+class RowMap(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_int32), ("dst", ctypes.c_int32), ("len", ctypes.c_int32)]
 
 
 _SIGNATURES = {
@@ -52,6 +56,12 @@ _SIGNATURES = {
     "docmask_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "docmask_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "docmask_kernel_class_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "docmask_copy_rows": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _i32, ctypes.c_int, _vp]),
+    "docmask_exchange_send_maps": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _i32, ctypes.POINTER(_i32),
+                                                  ctypes.POINTER(_i64)]),
+    "docmask_exchange_recv_maps": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i64, ctypes.POINTER(_i32),
+                                                  ctypes.POINTER(_i32), _vp, _i32, ctypes.POINTER(_i32), _vp, _i32,
+                                                  ctypes.POINTER(_i32)]),
 }
 
 
@@ -262,3 +272,71 @@ def timing_read(kernel_class: int) -> tuple[float, int]:
 
 def kernel_class_name(kernel_class: int) -> str:
     return lib().docmask_kernel_class_name(kernel_class).decode()
+
+
+# ----------------------------------------------------------------- KV exchange
+def _host_i32(x):
+    a = (ctypes.c_int32 * max(len(x), 1))()
+    for i, v in enumerate(x):
+        a[i] = int(v)
+    return a
+
+
+def _maps_arr(maps):
+    n = len(maps)
+    arr = (RowMap * max(n, 1))()
+    for i, (s_, d_, l_) in enumerate(maps):
+        arr[i].src, arr[i].dst, arr[i].len = int(s_), int(d_), int(l_)
+    return arr, n
+
+
+def _maps_list(arr, n):
+    return [(arr[i].src, arr[i].dst, arr[i].len) for i in range(n)]
+
+
+def copy_rows(src_k, src_v, dst_k, dst_v, maps, zero_gaps: bool):
+    """dst[m.dst + t] = src[m.src + t] for every (src, dst, len) map, rows of
+    the tensors' first dimension; K and V together or src_v = dst_v = None."""
+    row_bytes = src_k[0].numel() * src_k.element_size() if src_k.shape[0] else \
+        dst_k[0].numel() * dst_k.element_size()
+    for t in (src_k, src_v, dst_k, dst_v):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("copy_rows needs contiguous tensors")
+    if dst_k[0].numel() * dst_k.element_size() != row_bytes:
+        raise ValueError("source and destination rows differ in size")
+    arr, n = _maps_arr(maps)
+    _check(lib().docmask_copy_rows(_ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k), _ptr(dst_v),
+                                   dst_k.shape[0], row_bytes, arr, n, 1 if zero_gaps else 0, _stream()),
+           "docmask_copy_rows")
+
+
+def exchange_send_maps(cu_seqlens_host, chunks):
+    """(maps, send_rows): local KV rows -> packed send buffer for one worker."""
+    cu = _host_i32(cu_seqlens_host)
+    arr, n = _chunks(chunks)
+    nm, rows = _i32(0), _i64(0)
+    _check(lib().docmask_exchange_send_maps(cu, len(cu_seqlens_host) - 1, arr, n, None, 0, ctypes.byref(nm),
+                                            ctypes.byref(rows)), "docmask_exchange_send_maps")
+    out = (RowMap * max(nm.value, 1))()
+    _check(lib().docmask_exchange_send_maps(cu, len(cu_seqlens_host) - 1, arr, n, out, nm.value, ctypes.byref(nm),
+                                            ctypes.byref(rows)), "docmask_exchange_send_maps")
+    return _maps_list(out, nm.value), int(rows.value)
+
+
+def exchange_recv_maps(cu_seqlens_host, rank_chunks, rank: int, slot_rows: int):
+    """dict(kv_lo, kv_hi, remote, local) for worker `rank` (see docmask.h)."""
+    cu = _host_i32(cu_seqlens_host)
+    flat = [c for ch in rank_chunks for c in ch]
+    arr, _ = _chunks(flat)
+    counts = _host_i32([len(ch) for ch in rank_chunks])
+    lo, hi, nr, nl = _i32(0), _i32(0), _i32(0), _i32(0)
+    args = (cu, len(cu_seqlens_host) - 1, arr, counts, len(rank_chunks), rank, slot_rows, ctypes.byref(lo),
+            ctypes.byref(hi))
+    _check(lib().docmask_exchange_recv_maps(*args, None, 0, ctypes.byref(nr), None, 0, ctypes.byref(nl)),
+           "docmask_exchange_recv_maps")
+    rem = (RowMap * max(nr.value, 1))()
+    loc = (RowMap * max(nl.value, 1))()
+    _check(lib().docmask_exchange_recv_maps(*args, rem, nr.value, ctypes.byref(nr), loc, nl.value, ctypes.byref(nl)),
+           "docmask_exchange_recv_maps")
+    return {"kv_lo": lo.value, "kv_hi": hi.value, "remote": _maps_list(rem, nr.value),
+            "local": _maps_list(loc, nl.value)}

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "common.h"
+#include "docmask.h"
 #include "timing.h"
 
 namespace docmask {
@@ -86,5 +87,8 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t stream);
 int dq_rows_per_tile(int group);
+hipError_t launch_copy_rows(const void* src_k, const void* src_v, void* dst_k, void* dst_v, int64_t dst_rows,
+                            int64_t row_bytes, const docmask_rowmap* maps, int32_t n_maps, bool zero_gaps,
+                            hipStream_t stream);
 
 }  // namespace docmask

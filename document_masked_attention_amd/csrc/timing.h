@@ -18,7 +18,8 @@ enum KernelClass {
   KC_DQ = 4,
   KC_MERGE = 5,
   KC_CONVERT = 6,
-  KC_COUNT = 7
+  KC_COPY = 7,       // KV exchange row copies
+  KC_COUNT = 8
 };
 
 bool timing_enabled();

@@ -265,6 +265,20 @@ def per_doc_chunks(lengths, cp: int, rank: int) -> list:
     return out
 
 
+def random_plan(rng: np.random.Generator, total: int, n_ranks: int, n_cuts: int) -> list:
+    """A random assignment of the sequence to workers: [0, total) cut at
+    n_cuts random points, each piece given to a random worker (every worker
+    gets at least one piece when there are enough); per worker the pieces in
+    ascending order, adjacent ones kept separate.  Covers every token once."""
+    cuts = sorted(set(int(x) for x in rng.integers(1, max(total, 2), size=n_cuts) if 0 < x < total))
+    bounds = [0] + cuts + [total]
+    pieces = [(bounds[i], bounds[i + 1] - bounds[i]) for i in range(len(bounds) - 1) if bounds[i + 1] > bounds[i]]
+    owner = rng.integers(0, n_ranks, size=len(pieces))
+    if len(pieces) >= n_ranks:
+        owner[rng.permutation(len(pieces))[:n_ranks]] = np.arange(n_ranks)
+    return [[p for p, o in zip(pieces, owner) if o == r] for r in range(n_ranks)]
+
+
 FIG3_PATTERNS = ("1x131072", "16x8192", "bimodal131072")
 
 

@@ -168,6 +168,69 @@ int docmask_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_t stre
 
 const char* docmask_strerror(int status);
 
+/* ------------------------------------------------------------------------
+ * KV exchange of sharding-aware context parallelism (FlashCP section 3.2,
+ * "Dynamic Sharding-aware Communication", and Eq. 5): a worker sends only the
+ * KV rows of its document shards that are not the last shard of their
+ * document (a document kept whole on one worker is its own last shard),
+ * compacted into one continuous buffer with no per-document padding; the
+ * collective itself is the caller's.  A receiving worker places the rows its
+ * chunks need, and its own rows, at their global positions in the KV range
+ * [kv_lo, kv_hi) the attention entry points take.  Shards are the
+ * intersections of a worker's chunks with documents.
+ *
+ * Row maps are host arrays: rows [src, src + len) of a source go to rows
+ * [dst, dst + len) of a destination.
+ */
+typedef struct {
+  int32_t src;
+  int32_t dst;
+  int32_t len;
+} docmask_rowmap;
+
+/* Copies rows by a map list: dst[m.dst + t] = src[m.src + t] for every map m
+ * and t < m.len, for one tensor (src_v = dst_v = NULL) or two (K and V, same
+ * maps).  Rows are row_bytes long (a positive multiple of 16; Hkv * D * 2 for
+ * bf16 KV).  Maps must be sorted by dst and disjoint there, with len >= 0 and
+ * every row inside [0, src_rows) and [0, dst_rows); any number of maps (one
+ * launch per 128).  zero_gaps != 0 also zeroes every destination row that no
+ * map covers, so that the whole of [0, dst_rows) is written; otherwise those
+ * rows are left untouched.  Source and destination must not overlap; tensor
+ * pointers 16-byte aligned.  Bandwidth bound: covered rows are read once and
+ * every written row is written once. */
+int docmask_copy_rows(const void* src_k, const void* src_v, int64_t src_rows, void* dst_k, void* dst_v,
+                      int64_t dst_rows, int64_t row_bytes, const docmask_rowmap* maps, int32_t n_maps,
+                      int zero_gaps, hipStream_t stream);
+
+/* Send side, host only.  For one worker's chunk list (ascending, disjoint,
+ * inside the sequence) and host cu_seqlens, the maps from its local KV rows
+ * (chunks concatenated) to the packed send buffer, in local order, coalesced
+ * where rows are contiguous in both; *send_rows = rows sent (the worker's
+ * term of Eq. 5's maximum).  maps = NULL only reports *n_maps and
+ * *send_rows; otherwise max_maps < *n_maps is DOCMASK_EINVAL. */
+int docmask_exchange_send_maps(const int32_t* cu_seqlens, int32_t n_docs, const docmask_chunk* chunks,
+                               int32_t n_chunks, docmask_rowmap* maps, int32_t max_maps, int32_t* n_maps,
+                               int64_t* send_rows);
+
+/* Receive side, host only.  all_chunks holds every worker's chunk list in
+ * worker order (worker k's rank_n_chunks[k] entries); together they must
+ * cover [0, cu_seqlens[n_docs]) exactly once (each token on one worker).  The
+ * gathered buffer holds worker k's packed rows at rows [k * slot_rows, ...);
+ * slot_rows must be at least every worker's send_rows.  For worker `rank`:
+ * *kv_lo, *kv_hi = the KV range its chunks need (the document start of each
+ * chunk's first row up to the chunk end; 0, 0 without rows); `remote` = maps
+ * from the gathered buffer to rows of [kv_lo, kv_hi) (position - kv_lo),
+ * covering exactly the other workers' sent rows inside the need intervals,
+ * sorted by dst; `local` = maps from the worker's local KV rows to the same
+ * destination (one per non-empty chunk).  Copying `remote` with zero_gaps and
+ * then `local` without fills [kv_lo, kv_hi) with every row an allowed pair
+ * can reach and zeros elsewhere.  NULL map arrays only report counts;
+ * capacities below the counts are DOCMASK_EINVAL. */
+int docmask_exchange_recv_maps(const int32_t* cu_seqlens, int32_t n_docs, const docmask_chunk* all_chunks,
+                               const int32_t* rank_n_chunks, int32_t n_ranks, int32_t rank, int64_t slot_rows,
+                               int32_t* kv_lo, int32_t* kv_hi, docmask_rowmap* remote, int32_t max_remote,
+                               int32_t* n_remote, docmask_rowmap* local, int32_t max_local, int32_t* n_local);
+
 /* Kernel timing (instrumentation; defines no attention operation).
  * While enabled, every kernel launch of the library is bracketed by two HIP
  * events recorded on the launch stream, and their elapsed times are summed
@@ -188,7 +251,8 @@ enum {
   DOCMASK_KERNEL_DQ = 4,
   DOCMASK_KERNEL_MERGE = 5,
   DOCMASK_KERNEL_CONVERT = 6,
-  DOCMASK_N_KERNEL_CLASSES = 7
+  DOCMASK_KERNEL_COPY = 7,      /* docmask_copy_rows */
+  DOCMASK_N_KERNEL_CLASSES = 8
 };
 int docmask_timing_enable(int enable);
 int docmask_timing_read(int kernel_class, double* total_ms, int64_t* launches);

@@ -13,7 +13,9 @@ All arithmetic is float64 numpy.  Sources (web pages on context parallelism):
   Training" (FlashCP paper): section 2.1 and Figure 1(a) define the document
   mask (intra-document causal attention over a packed sequence); section 3.1
   gives the shard workload W = (2p + s + 1) * s / 2 (diagonal included);
-  section 2.2 gives the 2 x CP chunking.
+  section 2.2 gives the 2 x CP chunking; section 3.2 and Eq. 4 / Eq. 5 the
+  sharding-aware KV exchange (only shards that are not their document's last
+  shard travel, compacted into one buffer).
 * "LLM Context Parallel in Production" (production guide): the online-softmax
   combination of per-KV-block partial results keeps the row maximum and the
   exponential sum ("Core Principle: Split Q, Circulate KV"); block skipping and
@@ -32,6 +34,8 @@ force, finite differences, hand-derived fixtures in ``tests/golden/``).
 from .attention import (doc_index, local_positions, allowed_mask, attention_forward,
                         attention_backward, lse_merge)
 from .convert import round_to_bf16_bits
+from .exchange import (document_shards, is_last_shard, sent_rows, eq4_elements, eq5_elements,
+                       packed_send_buffer, needed_positions, received_kv)
 from .schedule import (q_tiles, kv_tiles, tile_pair_counts_bruteforce, tile_pair_counts,
                        classify, schedule, need_intervals, useful_pairs, lpt_order)
 
@@ -39,4 +43,6 @@ __all__ = [
     "doc_index", "local_positions", "allowed_mask", "attention_forward", "attention_backward",
     "lse_merge", "q_tiles", "kv_tiles", "tile_pair_counts_bruteforce", "tile_pair_counts",
     "classify", "schedule", "need_intervals", "useful_pairs", "lpt_order", "round_to_bf16_bits",
+    "document_shards", "is_last_shard", "sent_rows", "eq4_elements", "eq5_elements", "packed_send_buffer",
+    "needed_positions", "received_kv",
 ]

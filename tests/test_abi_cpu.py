@@ -113,3 +113,27 @@ def test_timing_controls(lib):
     assert lib.docmask_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == api.EINVAL
     assert lib.docmask_timing_read(api.N_KERNEL_CLASSES, ctypes.byref(ms), ctypes.byref(n)) == api.EINVAL
     assert lib.docmask_timing_read(0, None, ctypes.byref(n)) == api.EINVAL
+
+
+def _copy(lib, maps=((0, 0, 4),), src_k=FAKE, src_v=FAKE, dst_k=FAKE, dst_v=FAKE, src_rows=10, dst_rows=10,
+          row_bytes=64, zero=0):
+    arr, n = api._maps_arr(list(maps))
+    return lib.docmask_copy_rows(src_k, src_v, src_rows, dst_k, dst_v, dst_rows, row_bytes, arr, n, zero, None)
+
+
+def test_copy_rows_validation(lib):
+    assert _copy(lib, row_bytes=40) == api.EINVAL                       # not a multiple of 16
+    assert _copy(lib, row_bytes=0) == api.EINVAL
+    assert _copy(lib, maps=((0, 4, 4), (0, 2, 4))) == api.EINVAL        # destinations not ascending
+    assert _copy(lib, maps=((0, 0, 4), (0, 3, 2))) == api.EINVAL        # overlapping destinations
+    assert _copy(lib, maps=((8, 0, 4),)) == api.EINVAL                  # source past its end
+    assert _copy(lib, maps=((0, 8, 4),)) == api.EINVAL                  # destination past its end
+    assert _copy(lib, maps=((-1, 0, 4),)) == api.EINVAL
+    assert _copy(lib, maps=((0, 0, -1),)) == api.EINVAL
+    assert _copy(lib, src_v=None) == api.EINVAL                         # K and V must come together
+    assert _copy(lib, dst_k=MIS) == api.EINVAL
+    assert _copy(lib, src_k=None) == api.EINVAL
+    assert _copy(lib, dst_rows=-1) == api.EINVAL
+    assert _copy(lib, maps=()) == api.OK                                # nothing to write
+    assert _copy(lib, maps=((0, 0, 0),)) == api.OK                      # empty map only
+    assert _copy(lib, maps=(), dst_rows=0, zero=1) == api.OK
