@@ -393,6 +393,83 @@ def bench_merge(api, torch, dev, upload, steps):
     return merge, cp_fwd
 
 
+def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps):
+    """Sharding-aware KV exchange of every worker (FlashCP section 3.2): rows
+    sent (Eq. 5's terms) against the static full-KV pattern (Eq. 4), and the
+    time of the two copies one GPU runs: packing the worker's sent rows, and
+    placing the gathered rows plus its own at their positions."""
+    from document_masked_attention_amd.workloads import fig3_workload, cu_from_lengths
+    cu = cu_from_lengths(lengths)
+    total = int(cu[-1])
+    rb = hkv * d * 2                                   # bytes per KV row and tensor
+    out = {}
+    for sharding in ("per_sequence", "per_doc"):
+        plan = [fig3_workload("", sharding, cp, r, hq, hkv, d, seed, lengths=lengths).chunks for r in range(cp)]
+        send = [api.exchange_send_maps(cu, ch) for ch in plan]
+        slot = max([n for _, n in send] + [1])
+        gk = torch.zeros((cp * slot, hkv, d), dtype=torch.bfloat16, device=dev)
+        gv = torch.zeros_like(gk)
+        pack_ms, unpack_ms, pack_bytes, unpack_bytes = [], [], [], []
+        locs = []
+        for r, ch in enumerate(plan):
+            pos = torch.as_tensor(np.concatenate([np.arange(g, g + n) for g, n in ch]), device=dev)
+            kl, vl = kf.index_select(0, pos), vf.index_select(0, pos)
+            locs.append((kl, vl))
+            maps, n = send[r]
+            dk, dv = gk[r * slot:r * slot + n], gv[r * slot:r * slot + n]
+
+            def pack():
+                api.copy_rows(kl, vl, dk, dv, maps, False)
+            pack()
+            torch.cuda.synchronize()
+            api.timing_enable(True)
+            for _ in range(reps):
+                pack()
+            torch.cuda.synchronize()
+            pack_ms.append(api.timing_read(api.KERNEL_COPY)[0] / reps)
+            api.timing_enable(False)
+            pack_bytes.append(2 * 2 * n * rb)
+        for r, ch in enumerate(plan):
+            m = api.exchange_recv_maps(cu, plan, r, slot)
+            span = m["kv_hi"] - m["kv_lo"]
+            bk = torch.empty((span, hkv, d), dtype=torch.bfloat16, device=dev)
+            bv = torch.empty_like(bk)
+            kl, vl = locs[r]
+
+            def place():
+                api.copy_rows(gk, gv, bk, bv, m["remote"], True)
+                api.copy_rows(kl, vl, bk, bv, m["local"], False)
+            place()
+            torch.cuda.synchronize()
+            api.timing_enable(True)
+            for _ in range(reps):
+                place()
+            torch.cuda.synchronize()
+            unpack_ms.append(api.timing_read(api.KERNEL_COPY)[0] / reps)
+            api.timing_enable(False)
+            remote_rows = sum(x[2] for x in m["remote"])
+            own = sum(x[2] for x in m["local"])
+            unpack_bytes.append(2 * rb * (remote_rows + span + 2 * own))
+            del bk, bv
+        sent = [n for _, n in send]
+        eq4 = 4.0 * total / cp * hkv * d * (cp - 1) * 2
+        eq5 = 4.0 * max(sent) * hkv * d * (cp - 1) * 2
+        pb, pm = np.array(pack_bytes, float), np.array(pack_ms)
+        ub, um = np.array(unpack_bytes, float), np.array(unpack_ms)
+        out[sharding] = {
+            "sent_rows_per_rank": sent, "eq4_bytes": eq4, "eq5_bytes": eq5, "eq5_over_eq4": round(eq5 / eq4, 4),
+            "pack_ms_per_rank": [round(x, 4) for x in pm], "unpack_ms_per_rank": [round(x, 4) for x in um],
+            "pack_GBps": round(float(pb.sum() / (pm.sum() * 1e-3) / 1e9), 1) if pm.sum() > 0 else None,
+            "unpack_GBps": round(float(ub.sum() / (um.sum() * 1e-3) / 1e9), 1),
+            "unpack_frac_of_hbm_peak": round(float(ub.sum() / (um.sum() * 1e-3) / 1e9 / PEAK_HBM_GBS), 4),
+            "bytes_note": "pack: K and V sent rows read + written; place: gathered rows read, the whole KV range "
+                          "written (zeros between), own rows read + written"}
+        log(f"[study] exchange {sharding}: eq5/eq4 {eq5 / eq4:.3f}, pack {out[sharding]['pack_GBps']} GB/s, "
+            f"place {out[sharding]['unpack_GBps']} GB/s")
+        del gk, gv, locs
+    return out
+
+
 def study_sharding(cp: int, reps: int):
     """Kernel-efficiency study of 2 x CP sharding on one GPU (the single-GPU
     analogue of FlashCP Figure 3).  For every rank r of a CP group of size cp,
@@ -501,7 +578,9 @@ def study_sharding(cp: int, reps: int):
                        "pair_imbalance": round(float(pr.max() / pr.mean()), 4),
                        "mean_rank_tflops": round(float((flop / (ms * 1e-3)).mean() / 1e12), 2),
                        "mean_rank_frac_of_peak": round(float((flop / (ms * 1e-3)).mean() / 1e12 / PEAK_BF16_TFLOPS), 4)})
-        out["patterns"][pattern] = {"documents": len(lengths), **res}
+        out["patterns"][pattern] = {"documents": len(lengths), **res,
+                                    "exchange": exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d,
+                                                               seed, reps)}
         del qf, kf, vf
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)

@@ -297,13 +297,15 @@ def _maps_list(arr, n):
 def copy_rows(src_k, src_v, dst_k, dst_v, maps, zero_gaps: bool):
     """dst[m.dst + t] = src[m.src + t] for every (src, dst, len) map, rows of
     the tensors' first dimension; K and V together or src_v = dst_v = None."""
-    row_bytes = src_k[0].numel() * src_k.element_size() if src_k.shape[0] else \
-        dst_k[0].numel() * dst_k.element_size()
+    def row_bytes_of(t):
+        return math.prod(t.shape[1:]) * t.element_size()
+
+    row_bytes = row_bytes_of(src_k)
     for t in (src_k, src_v, dst_k, dst_v):
         if t is not None and not t.is_contiguous():
             raise ValueError("copy_rows needs contiguous tensors")
-    if dst_k[0].numel() * dst_k.element_size() != row_bytes:
-        raise ValueError("source and destination rows differ in size")
+        if t is not None and row_bytes_of(t) != row_bytes:
+            raise ValueError("source and destination rows differ in size")
     arr, n = _maps_arr(maps)
     _check(lib().docmask_copy_rows(_ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k), _ptr(dst_v),
                                    dst_k.shape[0], row_bytes, arr, n, 1 if zero_gaps else 0, _stream()),

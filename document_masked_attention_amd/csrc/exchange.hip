@@ -40,7 +40,7 @@ struct CopyTable {
 
 struct CopyParams {
   const u32x4* src_k;
-  const u32x4* src_v;               // null: one tensor
+  const u32x4* src_v;               // null: one tensor (or no map)
   u32x4* dst_k;
   u32x4* dst_v;
   int64_t row_units;                // 16-byte units per row
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(CopyParams p, C
   const int64_t ru = p.row_units;
   const int64_t span = (int64_t)kCopyThreads * kCopyUnroll;
   const int64_t dst0 = p.row0 * ru;
-  const bool two = p.src_v != nullptr;
+  const bool two = p.dst_v != nullptr;            // a source V exists whenever a map does
   for (int64_t c0 = (int64_t)blockIdx.x * span; c0 < p.n_units; c0 += (int64_t)gridDim.x * span) {
     const int64_t r_first = c0 / ru;
     int lo = 0, hi = n;                             // first map ending after the span's first row
@@ -225,7 +225,6 @@ int docmask_copy_rows(const void* src_k, const void* src_v, int64_t src_rows, vo
   if (row_bytes <= 0 || row_bytes % 16 || src_rows < 0 || dst_rows < 0 || n_maps < 0) return DOCMASK_EINVAL;
   if (src_rows > INT32_MAX || dst_rows > INT32_MAX) return DOCMASK_EINVAL;
   if (n_maps > 0 && !maps) return DOCMASK_EINVAL;
-  if ((src_v == nullptr) != (dst_v == nullptr)) return DOCMASK_EINVAL;
   std::vector<docmask_rowmap> m;
   m.reserve(n_maps);
   int64_t prev_end = 0;
@@ -237,7 +236,8 @@ int docmask_copy_rows(const void* src_k, const void* src_v, int64_t src_rows, vo
     if (r.len > 0) m.push_back(r);
   }
   const bool writes = dst_rows > 0 && (!m.empty() || zero_gaps);
-  if (!writes) return DOCMASK_OK;
+  if (!writes) return DOCMASK_OK;                 // empty tensors may come with null pointers
+  if ((src_v == nullptr) != (dst_v == nullptr) && !(m.empty() && src_v == nullptr)) return DOCMASK_EINVAL;
   if (!dst_k || !aligned16(dst_k) || (dst_v && !aligned16(dst_v))) return DOCMASK_EINVAL;
   if (!m.empty() && (!src_k || !aligned16(src_k) || (src_v && !aligned16(src_v)))) return DOCMASK_EINVAL;
   const hipError_t e = launch_copy_rows(src_k, src_v, dst_k, dst_v, dst_rows, row_bytes, m.data(),

@@ -295,10 +295,11 @@ def fig3_lengths(pattern: str, seed: int = 5) -> list:
 
 
 def fig3_workload(pattern: str, sharding: str, cp: int, rank: int, hq: int = 32, hkv: int = 8, d: int = 128,
-                  seed: int = 5) -> Workload:
+                  seed: int = 5, lengths=None) -> Workload:
     """One CP rank's forward under per-sequence or per-document 2 x CP sharding,
-    attending the whole (all-gathered) KV range."""
-    lengths = fig3_lengths(pattern, seed)
+    attending the whole (all-gathered) KV range; ``lengths`` overrides the
+    pattern's documents."""
+    lengths = fig3_lengths(pattern, seed) if lengths is None else list(lengths)
     total = int(sum(lengths))
     if sharding == "per_sequence":
         chunks = sequence_zigzag_chunks(total, cp, rank)

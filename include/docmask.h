@@ -196,7 +196,8 @@ typedef struct {
  * launch per 128).  zero_gaps != 0 also zeroes every destination row that no
  * map covers, so that the whole of [0, dst_rows) is written; otherwise those
  * rows are left untouched.  Source and destination must not overlap; tensor
- * pointers 16-byte aligned.  Bandwidth bound: covered rows are read once and
+ * pointers 16-byte aligned; a call that writes nothing (dst_rows = 0, or no
+ * map and no zeroing) checks no pointer.  Bandwidth bound: covered rows are read once and
  * every written row is written once. */
 int docmask_copy_rows(const void* src_k, const void* src_v, int64_t src_rows, void* dst_k, void* dst_v,
                       int64_t dst_rows, int64_t row_bytes, const docmask_rowmap* maps, int32_t n_maps,
