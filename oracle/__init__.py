@@ -15,7 +15,8 @@ All arithmetic is float64 numpy.  Sources (web pages on context parallelism):
   gives the shard workload W = (2p + s + 1) * s / 2 (diagonal included);
   section 2.2 gives the 2 x CP chunking; section 3.2 and Eq. 4 / Eq. 5 the
   sharding-aware KV exchange (only shards that are not their document's last
-  shard travel, compacted into one buffer).
+  shard travel, compacted into one buffer); section 3.3 and Algorithm 1 the
+  Whole-Doc / Per-Doc heuristic planner.
 * "LLM Context Parallel in Production" (production guide): the online-softmax
   combination of per-KV-block partial results keeps the row maximum and the
   exponential sum ("Core Principle: Split Q, Circulate KV"); block skipping and
@@ -36,6 +37,7 @@ from .attention import (doc_index, local_positions, allowed_mask, attention_forw
 from .convert import round_to_bf16_bits
 from .exchange import (document_shards, is_last_shard, sent_rows, eq4_elements, eq5_elements,
                        packed_send_buffer, needed_positions, received_kv)
+from .planner import shard_workload, flashcp_plan, plan_chunks, imbalance_ratio
 from .schedule import (q_tiles, kv_tiles, tile_pair_counts_bruteforce, tile_pair_counts,
                        classify, schedule, need_intervals, useful_pairs, lpt_order)
 
@@ -44,5 +46,5 @@ __all__ = [
     "lse_merge", "q_tiles", "kv_tiles", "tile_pair_counts_bruteforce", "tile_pair_counts",
     "classify", "schedule", "need_intervals", "useful_pairs", "lpt_order", "round_to_bf16_bits",
     "document_shards", "is_last_shard", "sent_rows", "eq4_elements", "eq5_elements", "packed_send_buffer",
-    "needed_positions", "received_kv",
+    "needed_positions", "received_kv", "shard_workload", "flashcp_plan", "plan_chunks", "imbalance_ratio",
 ]
