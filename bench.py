@@ -393,6 +393,17 @@ def bench_merge(api, torch, dev, upload, steps):
     return merge, cp_fwd
 
 
+FLASHCP_RATIO = 1.05         # target workload ratio of the planner in the sharding study
+
+
+def study_plan(api, sharding, lengths, cp, hq, hkv, d, seed):
+    """Every worker's chunk list under one sharding of the study."""
+    from document_masked_attention_amd.workloads import fig3_workload
+    if sharding == "flashcp":
+        return api.plan_shards(lengths, cp, FLASHCP_RATIO)[0]
+    return [fig3_workload("", sharding, cp, r, hq, hkv, d, seed, lengths=lengths).chunks for r in range(cp)]
+
+
 def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps):
     """Sharding-aware KV exchange of every worker (FlashCP section 3.2): rows
     sent (Eq. 5's terms) against the static full-KV pattern (Eq. 4), and the
@@ -403,8 +414,8 @@ def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps)
     total = int(cu[-1])
     rb = hkv * d * 2                                   # bytes per KV row and tensor
     out = {}
-    for sharding in ("per_sequence", "per_doc"):
-        plan = [fig3_workload("", sharding, cp, r, hq, hkv, d, seed, lengths=lengths).chunks for r in range(cp)]
+    for sharding in ("per_sequence", "per_doc", "flashcp"):
+        plan = study_plan(api, sharding, lengths, cp, hq, hkv, d, seed)
         send = [api.exchange_send_maps(cu, ch) for ch in plan]
         slot = max([n for _, n in send] + [1])
         gk = torch.zeros((cp * slot, hkv, d), dtype=torch.bfloat16, device=dev)
@@ -479,14 +490,17 @@ def study_sharding(cp: int, reps: int):
       per_doc             pieces r and 2cp-1-r of every document, one call;
       per_doc_blockwise   the same rows computed block by block, one call per
                           contiguous KV block of T/cp keys that the rows need,
-                          then the partials merged (ring-style execution).
+                          then the partials merged (ring-style execution);
+      flashcp             the library's Algorithm 1 plan (whole documents, head
+                          cuts for equal tokens, Per-Doc for the longest ones
+                          while the workload ratio exceeds 1.05), one call.
 
     Time per rank = the library's event timer summed over scheduler, forward
     and merge kernels; a CP step is as slow as its slowest rank."""
     import torch
     from document_masked_attention_amd import api
-    from document_masked_attention_amd.workloads import (FIG3_PATTERNS, fig3_lengths, fig3_workload, draw_tensor,
-                                                         cu_from_lengths)
+    from document_masked_attention_amd.workloads import (FIG3_PATTERNS, fig3_lengths, draw_tensor, cu_from_lengths,
+                                                         Workload)
     api.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -511,11 +525,21 @@ def study_sharding(cp: int, reps: int):
         cu = torch.as_tensor(cu_from_lengths(lengths), dtype=torch.int32, device=dev)
         blk = total // cp
         res = {s: {"per_rank_ms": [], "per_rank_wall_ms": [], "per_rank_pairs": [], "per_rank_chunks": []}
-               for s in ("per_sequence", "per_doc", "per_doc_blockwise")}
+               for s in ("per_sequence", "per_doc", "per_doc_blockwise", "flashcp")}
+        plans = {sh: study_plan(api, sh, lengths, cp, hq, hkv, d, seed) for sh in ("per_sequence", "per_doc", "flashcp")}
         scale = 1.0 / np.sqrt(d)
+        # the GPU idled while the inputs were generated: bring its clocks up before timing rank 0
+        wq = qf.index_select(0, torch.arange(16384, device=dev))
+        t_end = time.time() + 1.0
+        while time.time() < t_end:
+            for _ in range(10):
+                api.attn_fwd(wq, kf, vf, cu, [(0, 16384)], 0, total, scale)
+            torch.cuda.synchronize()
+        del wq
         for r in range(cp):
-            for sharding in ("per_sequence", "per_doc"):
-                w = fig3_workload(pattern, sharding, cp, r, hq, hkv, d, seed)
+            for sharding in ("per_sequence", "per_doc", "flashcp"):
+                w = Workload(f"{sharding}_cp{cp}_rank{r}_{pattern}", seed, total, lengths, hq, hkv, d,
+                             plans[sharding][r], 0, total)
                 pos = torch.as_tensor(w.local_positions(), device=dev)
                 q = qf.index_select(0, pos)
                 o = torch.empty((w.tq, hq, d), dtype=torch.bfloat16, device=dev)

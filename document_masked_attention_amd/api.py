@@ -56,6 +56,8 @@ _SIGNATURES = {
     "docmask_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "docmask_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "docmask_kernel_class_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "docmask_plan_shards": (ctypes.c_int, [_vp, _i32, _i32, ctypes.c_double, _vp, _i32, _vp, _vp,
+                                           ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)]),
     "docmask_copy_rows": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _i32, ctypes.c_int, _vp]),
     "docmask_exchange_send_maps": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _i32, ctypes.POINTER(_i32),
                                                   ctypes.POINTER(_i64)]),
@@ -342,3 +344,23 @@ def exchange_recv_maps(cu_seqlens_host, rank_chunks, rank: int, slot_rows: int):
            "docmask_exchange_recv_maps")
     return {"kv_lo": lo.value, "kv_hi": hi.value, "remote": _maps_list(rem, nr.value),
             "local": _maps_list(loc, nl.value)}
+
+
+def plan_shards(doc_lengths, n_workers: int, target_ratio: float):
+    """FlashCP planner: (per-worker chunk lists, Per-Doc document ids, ratio)."""
+    lens = _host_i32(doc_lengths)
+    n = len(doc_lengths)
+    counts = (ctypes.c_int32 * n_workers)()
+    npd, ratio = _i32(0), ctypes.c_double(0.0)
+    pd = (ctypes.c_int32 * max(n, 1))()
+    _check(lib().docmask_plan_shards(lens, n, n_workers, target_ratio, None, 0, counts, pd, ctypes.byref(npd),
+                                     ctypes.byref(ratio)), "docmask_plan_shards")
+    total = sum(counts)
+    arr = (Chunk * max(total, 1))()
+    _check(lib().docmask_plan_shards(lens, n, n_workers, target_ratio, arr, total, counts, pd, ctypes.byref(npd),
+                                     ctypes.byref(ratio)), "docmask_plan_shards")
+    out, k = [], 0
+    for j in range(n_workers):
+        out.append([(arr[k + i].g_start, arr[k + i].len) for i in range(counts[j])])
+        k += counts[j]
+    return out, [pd[i] for i in range(npd.value)], ratio.value

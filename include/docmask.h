@@ -203,6 +203,28 @@ int docmask_copy_rows(const void* src_k, const void* src_v, int64_t src_rows, vo
                       int64_t dst_rows, int64_t row_bytes, const docmask_rowmap* maps, int32_t n_maps,
                       int zero_gaps, hipStream_t stream);
 
+/* Sharding planner, host only: FlashCP's heuristic (Algorithm 1, section
+ * 3.4) over documents of the given lengths (packed in this order) for
+ * n_workers CP workers and a target workload ratio R = max / mean >= 1.
+ * Documents stay whole (Whole-Doc sharding, section 3.3) and are cut only to
+ * equalise token counts (Eq. 2), head first; while the ratio exceeds R the
+ * longest remaining document switches to Per-Doc sharding (pieces i and
+ * 2N-1-i of 2N, section 2.3).  Shard workload W = (2p + s + 1) s / 2
+ * (section 3.1).  The pages leave two steps open; this library reads them
+ * as: a worker above its token target gives back its most recently added
+ * shards, and each goes to the least-loaded worker below its target, as
+ * much of its head as that worker lacks, the rest onward (ties always to the
+ * lowest worker index).
+ * Outputs: chunks = every worker's chunk list (global positions, ascending,
+ * adjacent shards joined) concatenated in worker order, worker_n_chunks[j]
+ * entries for worker j; per_doc (capacity n_docs, may be NULL) = ids of the
+ * Per-Doc documents, ascending, *n_per_doc of them; *ratio = the plan's
+ * workload ratio.  chunks = NULL only reports the counts; max_chunks below
+ * their sum is DOCMASK_EINVAL. */
+int docmask_plan_shards(const int32_t* doc_lengths, int32_t n_docs, int32_t n_workers, double target_ratio,
+                        docmask_chunk* chunks, int32_t max_chunks, int32_t* worker_n_chunks, int32_t* per_doc,
+                        int32_t* n_per_doc, double* ratio);
+
 /* Send side, host only.  For one worker's chunk list (ascending, disjoint,
  * inside the sequence) and host cu_seqlens, the maps from its local KV rows
  * (chunks concatenated) to the packed send buffer, in local order, coalesced

@@ -110,11 +110,14 @@ def _exchange(plan, lengths, hkv, d, seed):
     return cu, out
 
 
-@pytest.mark.parametrize("kind", ["per_doc", "per_sequence", "random"])
+@pytest.mark.parametrize("kind", ["per_doc", "per_sequence", "random", "flashcp"])
 def test_exchange_then_attention_small(kind):
-    rng = np.random.default_rng({"per_doc": 1, "per_sequence": 2, "random": 3}[kind])
+    rng = np.random.default_rng({"per_doc": 1, "per_sequence": 2, "random": 3, "flashcp": 4}[kind])
     n = 4
-    if kind == "per_sequence":
+    if kind == "flashcp":
+        lengths = [int(x) for x in rng.integers(1, 200, size=10)] + [900]
+        plan = oracle.plan_chunks(lengths, n, 1.05)[0]
+    elif kind == "per_sequence":
         lengths = [int(x) for x in rng.integers(1, 200, size=6)]
         lengths[-1] += (-sum(lengths)) % (2 * n)
         plan = [sequence_zigzag_chunks(sum(lengths), n, r) for r in range(n)]
@@ -146,3 +149,12 @@ def test_exchange_study_plan_full_size():
     D = 128): every worker's pack and placement bit-exact."""
     plan = [fig3_workload("16x8192", "per_doc", 8, r).chunks for r in range(8)]
     _exchange(plan, [8192] * 16, 8, 128, 5)
+
+
+def test_exchange_flashcp_plan_bimodal():
+    """The planner's CP = 8 plan of the bimodal 131072-token mix: every
+    worker's pack and placement bit-exact."""
+    from document_masked_attention_amd.workloads import bimodal_docs
+    lengths = bimodal_docs(5)
+    plan = oracle.plan_chunks(lengths, 8, 1.05)[0]
+    _exchange(plan, lengths, 8, 128, 5)

@@ -89,3 +89,22 @@ def test_blockwise_partials_merge():
                                               rows=sel)
     assert_close(o_np[sel], want_o, O_TOL, "merged O")
     assert_close(l_np[:, sel], want_l, LSE_TOL, "merged LSE")
+
+
+@pytest.mark.parametrize("rank", [0, 5])
+def test_flashcp_plan_sampled_rows(rank):
+    """A worker of the CP = 8 Algorithm 1 plan of the bimodal mix (whole
+    documents, head cuts, two Per-Doc documents): sampled rows vs the oracle."""
+    from document_masked_attention_amd.workloads import bimodal_docs
+    lengths = bimodal_docs(5)
+    chunks = oracle.plan_chunks(lengths, 8, 1.05)[0][rank]
+    w = custom_workload(5, lengths, 32, 8, 128, chunks=chunks)
+    print(f"[shard] flashcp rank {rank} chunks={len(chunks)} tq={w.tq}", flush=True)
+    q, k, v = w.q(), w.k(), w.v()
+    o, lse = api.attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.cu_seqlens, chunks, 0, w.total, w.scale)
+    torch.cuda.synchronize()
+    sel = _rows(w, 48, 13 + rank)
+    want_o, want_l = oracle.attention_forward(f64(q), f64(k), f64(v), w.cu_seqlens, chunks, 0, w.total, w.scale,
+                                              rows=sel)
+    assert_close(bf16_to_np(o)[sel], want_o, O_TOL, "O")
+    assert_close(lse.cpu().numpy()[:, sel], want_l, LSE_TOL, "LSE")
