@@ -387,6 +387,46 @@ def bench_merge(api, torch, dev, upload, steps):
                    "single_call_kernel_ms": round(one_ms, 4),
                    "single_call_tflops": round(flop / (one_ms * 1e-3) / 1e12, 2),
                    "single_call_frac_of_peak": round(flop / (one_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+    # the same per-block calls with float32 partials, merged by lse_merge_f32
+    jobs32 = []
+    for r0, g, n, blocks, po, pl in fwd_calls:
+        jobs32.append((r0, g, n, blocks, torch.empty(po.shape, dtype=torch.float32, device=dev), pl,
+                       torch.empty((n, w.hq, w.d), dtype=torch.bfloat16, device=dev),
+                       torch.empty((w.hq, n), dtype=torch.float32, device=dev)))
+
+    def fwd_all32():
+        for r0, g, n, blocks, po, pl, _, _ in jobs32:
+            for i, b in enumerate(blocks):
+                api.attn_fwd(q[r0:r0 + n], k[blk * b:blk * (b + 1)], v[blk * b:blk * (b + 1)], cu, [(g, n)],
+                             blk * b, blk * (b + 1), w.scale, out=po[i], lse=pl[i], f32_out=True)
+
+    def merge_all32():
+        for _, _, _, _, po, pl, oo, lo in jobs32:
+            api.lse_merge(po, pl, o_out=oo, lse_out=lo)
+
+    fwd_all32()
+    merge_all32()
+    torch.cuda.synchronize()
+    api.timing_enable(True)
+    for _ in range(reps):
+        fwd_all32()
+    torch.cuda.synchronize()
+    f32_fwd_ms = (api.timing_read(api.KERNEL_FWD)[0] + api.timing_read(api.KERNEL_SCHEDULE)[0]) / reps
+    api.timing_enable(False)
+    api.timing_enable(True)
+    for _ in range(reps):
+        merge_all32()
+    torch.cuda.synchronize()
+    f32_merge_ms = api.timing_read(api.KERNEL_MERGE)[0] / reps
+    api.timing_enable(False)
+    # the bf16 merge's bytes plus the second half of every float32 partial O row read
+    bytes32 = total_bytes + sum(int(torch.isfinite(j[5]).sum().item()) * 2 * w.d for j in jobs32)
+    cp_fwd.update({"f32_partials": {
+        "fwd_kernel_ms": round(f32_fwd_ms, 4), "merge_ms": round(f32_merge_ms, 4),
+        "total_ms": round(f32_fwd_ms + f32_merge_ms, 4), "merge_bytes": int(bytes32),
+        "merge_GBps": round(bytes32 / (f32_merge_ms * 1e-3) / 1e9, 1),
+        "note": "per-block forward calls writing float32 O, then lse_merge_f32 (bf16 output)"}})
+    del jobs32
     merge = {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
              "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
              "bound": "hbm"}

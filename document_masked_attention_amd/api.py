@@ -50,6 +50,9 @@ _SIGNATURES = {
     "docmask_attn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _f32, _vp, _vp, _vp, ctypes.c_int, _vp, _sz, _vp]),
     "lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "lse_merge_f32": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "docmask_attn_fwd_f32out": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                               _f32, _vp, _vp, _vp, _sz, _vp]),
     "docmask_check_errors": (ctypes.c_int, [_vp, _vp]),
     "docmask_f32_to_bf16": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
     "docmask_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -173,15 +176,18 @@ def schedule(cu_seqlens, chunks, kv_lo: int, kv_hi: int, bq: int, bk: int, devic
 
 
 def attn_fwd(q, k, v, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float | None = None,
-             out=None, lse=None, workspace=None):
-    """O [Tq, Hq, D] (bf16) and LSE [Hq, Tq] (float32) of document-masked attention."""
+             out=None, lse=None, workspace=None, f32_out: bool = False):
+    """O [Tq, Hq, D] (bf16; float32 with f32_out, for lse_merge_f32) and LSE
+    [Hq, Tq] (float32) of document-masked attention."""
     q, k, v = _bits(q), _bits(k), _bits(v)
     tq, hq, d = q.shape
     hkv = k.shape[1]
     cu = _dev_i32(cu_seqlens, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if out is None:
-        out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((tq, hq, d), dtype=torch.float32 if f32_out else torch.bfloat16, device=q.device)
+    if (out.dtype == torch.float32) != f32_out:
+        raise TypeError("out must be float32 exactly when f32_out is set")
     if lse is None:
         lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
     n_docs = cu.numel() - 1
@@ -191,9 +197,10 @@ def attn_fwd(q, k, v, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float |
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     arr, n = _chunks(chunks)
-    st = lib().docmask_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_docs, arr, n, kv_lo, kv_hi, hq, hkv, d,
-                                float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
-    _check(st, "docmask_attn_fwd")
+    fn = lib().docmask_attn_fwd_f32out if f32_out else lib().docmask_attn_fwd
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_docs, arr, n, kv_lo, kv_hi, hq, hkv, d,
+            float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "docmask_attn_fwd_f32out" if f32_out else "docmask_attn_fwd")
     return out, lse
 
 
@@ -233,16 +240,19 @@ def attn_bwd(q, k, v, o, lse, d_o, cu_seqlens, chunks, kv_lo: int, kv_hi: int, s
 
 
 def lse_merge(o_parts, lse_parts, o_out=None, lse_out=None):
-    """Merge partials o_parts [P, rows, hq, d] (bf16), lse_parts [P, hq, rows]."""
-    o_parts = _bits(o_parts)
+    """Merge partials o_parts [P, rows, hq, d] (bf16, or float32 from
+    attn_fwd(..., f32_out=True)), lse_parts [P, hq, rows]; bf16 output."""
+    f32 = o_parts.dtype == torch.float32
+    if not f32:
+        o_parts = _bits(o_parts)
     n_parts, rows, hq, d = o_parts.shape
     if o_out is None:
         o_out = torch.empty((rows, hq, d), dtype=torch.bfloat16, device=o_parts.device)
     if lse_out is None:
         lse_out = torch.empty((hq, rows), dtype=torch.float32, device=o_parts.device)
-    st = lib().lse_merge(_ptr(o_parts), _ptr(lse_parts), n_parts, rows, hq, d, _ptr(o_out), _ptr(lse_out),
-                         _stream())
-    _check(st, "lse_merge")
+    fn = lib().lse_merge_f32 if f32 else lib().lse_merge
+    st = fn(_ptr(o_parts), _ptr(lse_parts), n_parts, rows, hq, d, _ptr(o_out), _ptr(lse_out), _stream())
+    _check(st, "lse_merge_f32" if f32 else "lse_merge")
     return o_out, lse_out
 
 

@@ -185,16 +185,18 @@ int docmask_schedule(const int32_t* cu_seqlens_dev, int32_t n_docs, const docmas
   return hip_status(launch_schedule(p, lpt_q, lpt_kv, at<int32_t>(workspace, L.hist), stream));
 }
 
-int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
-                     int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
-                     int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o,
-                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// o (bf16) or o32 (float32): exactly one is the output of O
+static int attn_fwd_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                         int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo, int32_t kv_hi,
+                         int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o, float* o32, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Problem pr;
   int st = check_shape(n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, &pr);
   if (st != DOCMASK_OK) return st;
   if (!cu_seqlens_dev || !std::isfinite(softmax_scale)) return DOCMASK_EINVAL;
   if (pr.tq == 0) return DOCMASK_OK;
-  if (!q || !o || !lse || !aligned16(q) || !aligned16(o) || !aligned4(lse)) return DOCMASK_EINVAL;
+  void* out = o32 ? static_cast<void*>(o32) : o;
+  if (!q || !out || !lse || !aligned16(q) || !aligned16(out) || !aligned4(lse)) return DOCMASK_EINVAL;
   if (pr.tkv > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return DOCMASK_EINVAL;
   const Layout L = fwd_layout(chunks, n_chunks, pr);
   if (!workspace || workspace_bytes < L.total) return DOCMASK_EWORKSPACE;
@@ -219,6 +221,7 @@ int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
   fp.k = static_cast<const uint16_t*>(k);
   fp.v = static_cast<const uint16_t*>(v);
   fp.o = static_cast<uint16_t*>(o);
+  fp.o32 = o32;
   fp.lse = lse;
   fp.cu = cu_seqlens_dev;
   fp.plan = sp.plan_q;
@@ -228,6 +231,23 @@ int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
   fp.kv_lo = kv_lo; fp.kv_hi = kv_hi; fp.tq = (int32_t)pr.tq; fp.xcd_cluster = kXcdCluster;
   fp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   return hip_status(launch_fwd(fp, d, stream));
+}
+
+int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                     int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
+                     int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attn_fwd_impl(q, k, v, cu_seqlens_dev, n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, softmax_scale,
+                       o, nullptr, lse, workspace, workspace_bytes, stream);
+}
+
+int docmask_attn_fwd_f32out(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                            int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
+                            int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float* o,
+                            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!o) return DOCMASK_EINVAL;
+  return attn_fwd_impl(q, k, v, cu_seqlens_dev, n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, softmax_scale,
+                       nullptr, o, lse, workspace, workspace_bytes, stream);
 }
 
 int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -310,21 +330,35 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   return hip_status(launch_bwd(bp, d, (flags & DOCMASK_DELTA_READY) != 0, stream));
 }
 
-int lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,
-              int32_t d, void* o_out, float* lse_out, hipStream_t stream) {
+// o_parts (bf16) or o_parts32 (float32): exactly one holds the partials
+static int merge_impl(const void* o_parts, const float* o_parts32, const float* lse_parts, int32_t n_parts,
+                      int32_t rows, int32_t hq, int32_t d, void* o_out, float* lse_out, hipStream_t stream) {
   if (n_parts < 1 || rows < 0 || hq < 1) return DOCMASK_EINVAL;
   if (d != 64 && d != 128) return DOCMASK_EUNSUPPORTED;
   if ((int64_t)rows * hq > INT32_MAX) return DOCMASK_EINVAL;
   if (rows == 0) return DOCMASK_OK;
-  if (!o_parts || !lse_parts || !o_out || !lse_out) return DOCMASK_EINVAL;
-  if (!aligned16(o_parts) || !aligned16(o_out) || !aligned4(lse_parts) || !aligned4(lse_out)) return DOCMASK_EINVAL;
+  const void* parts = o_parts32 ? static_cast<const void*>(o_parts32) : o_parts;
+  if (!parts || !lse_parts || !o_out || !lse_out) return DOCMASK_EINVAL;
+  if (!aligned16(parts) || !aligned16(o_out) || !aligned4(lse_parts) || !aligned4(lse_out)) return DOCMASK_EINVAL;
   MergeParams p;
   p.o_parts = static_cast<const uint16_t*>(o_parts);
+  p.o_parts32 = o_parts32;
   p.lse_parts = lse_parts;
   p.o_out = static_cast<uint16_t*>(o_out);
   p.lse_out = lse_out;
   p.n_parts = n_parts; p.rows = rows; p.hq = hq;
   return hip_status(launch_merge(p, d, stream));
+}
+
+int lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,
+              int32_t d, void* o_out, float* lse_out, hipStream_t stream) {
+  return merge_impl(o_parts, nullptr, lse_parts, n_parts, rows, hq, d, o_out, lse_out, stream);
+}
+
+int lse_merge_f32(const float* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,
+                  int32_t d, void* o_out, float* lse_out, hipStream_t stream) {
+  if (!o_parts) return DOCMASK_EINVAL;
+  return merge_impl(nullptr, o_parts, lse_parts, n_parts, rows, hq, d, o_out, lse_out, stream);
 }
 
 int docmask_check_errors(const void* workspace, hipStream_t stream) {

@@ -274,10 +274,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   for (int u = 0; u + 1 < n; ++u) step(u, std::true_type{});
   if (n > 0) step(n - 1, std::false_type{});
 
-  // epilogue: normalise, write O (bf16) and LSE (natural log)
+  // epilogue: normalise, write O (bf16, or float32 partials) and LSE (natural log)
   const float l_tot = pair_sum32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row_ok) {
+  if (row_ok && p.o32) {
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 val = make_float4(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv, oacc[b][4 * g + 2] * inv,
+                                       oacc[b][4 * g + 3] * inv);
+        *reinterpret_cast<float4*>(p.o32 + o_off + 32 * b + 8 * g + 4 * hh) = val;
+      }
+  } else if (row_ok) {
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -289,6 +298,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         val.y = *reinterpret_cast<const uint32_t*>(&hi2);
         *reinterpret_cast<uint2*>(p.o + o_off + 32 * b + 8 * g + 4 * hh) = val;
       }
+  }
+  if (row_ok) {
     if (hh == 0)
       p.lse[(size_t)head * p.tq + l_row0 + qr] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }

@@ -30,6 +30,7 @@ struct FwdParams {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
+  float* o32;            // non-null: O written here as float32 (partials for the fp32 merge), o unused
   float* lse;
   const int32_t* cu;
   const int32_t* plan;   // [n_qtiles][QP_WORDS]
@@ -40,7 +41,8 @@ struct FwdParams {
 };
 
 struct MergeParams {
-  const uint16_t* o_parts;   // [P][rows][hq][D]
+  const uint16_t* o_parts;   // [P][rows][hq][D] bf16, or
+  const float* o_parts32;    // the same as float32 (non-null selects it)
   const float* lse_parts;    // [P][hq][rows]
   uint16_t* o_out;           // [rows][hq][D]
   float* lse_out;            // [hq][rows]

@@ -3,36 +3,47 @@
 // combined with the row maximum and the exponential sum).  Per row and head:
 //   m = max_p LSE_p,  LSE = m + ln sum_p exp(LSE_p - m),
 //   O = sum_p exp(LSE_p - LSE) O_p;   every partial empty -> (0, -inf).
-// Bandwidth bound: every thread streams one 16-byte slice (8 bf16) of one
-// (row, head) from each partial whose LSE is finite, and writes one slice.
+// Bandwidth bound: every thread streams one slice of 8 values of one (row,
+// head) from each partial whose LSE is finite (16 bytes of bf16, or 32 bytes
+// when the partials are float32), and writes one 16-byte bf16 slice.
 #include "kernels.h"
 
 namespace docmask {
 
-// Weighted sum of the 16-byte slices of partials [q0, q0 + QB) with LSE values
-// lq (-inf: empty partial, weight 0, not read); all slices are requested
-// before any is used.
-template <int QB>
+// Weighted sum of the slices of partials [q0, q0 + QB) with LSE values lq
+// (-inf: empty partial, weight 0, not read); all slices are requested before
+// any is used.  op points at the thread's slice of partial 0 in 16-byte units
+// (two units per slice for float32 partials); o_stride = units between partials.
+template <int QB, bool F32>
 __device__ __forceinline__ void merge_group(const u32x4* op, size_t o_stride, int q0, const float (&lq)[QB],
                                             float lse2, float (&acc)[8]) {
+  constexpr int U = F32 ? 2 : 1;
   float wgt[QB];
-  u32x4 raw[QB];
+  u32x4 raw[QB][U];
 #pragma unroll
   for (int i = 0; i < QB; ++i) {
     wgt[i] = lq[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i], kLog2e, -lse2));
-    raw[i] = u32x4{0u, 0u, 0u, 0u};
-    if (lq[i] != -INFINITY) raw[i] = __builtin_nontemporal_load(op + (size_t)(q0 + i) * o_stride);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      raw[i][j] = u32x4{0u, 0u, 0u, 0u};
+      if (lq[i] != -INFINITY) raw[i][j] = __builtin_nontemporal_load(op + (size_t)(q0 + i) * o_stride + j);
+    }
   }
 #pragma unroll
   for (int i = 0; i < QB; ++i)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      acc[2 * k] += wgt[i] * __uint_as_float(raw[i][k] << 16);
-      acc[2 * k + 1] += wgt[i] * __uint_as_float(raw[i][k] & 0xffff0000u);
+      if (F32) {
+        acc[k] += wgt[i] * __uint_as_float(raw[i][0][k]);
+        acc[4 + k] += wgt[i] * __uint_as_float(raw[i][U - 1][k]);
+      } else {
+        acc[2 * k] += wgt[i] * __uint_as_float(raw[i][0][k] << 16);
+        acc[2 * k + 1] += wgt[i] * __uint_as_float(raw[i][0][k] & 0xffff0000u);
+      }
     }
 }
 
-template <int D>
+template <int D, bool F32>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   constexpr int CPR = D / 8;                        // threads per (row, head)
   constexpr int QB = 8;                             // partials per batch of loads
@@ -45,8 +56,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const size_t lse_stride = n_rh;                   // elements between partials
   const float* lp = p.lse_parts + (size_t)head * p.rows + row;
   const int np = p.n_parts;
-  const u32x4* op = reinterpret_cast<const u32x4*>(p.o_parts + rh * D + 8 * c);
-  const size_t o_stride = n_rh * D / 8;             // 16-byte slices between partials
+  const u32x4* op = F32 ? reinterpret_cast<const u32x4*>(p.o_parts32 + rh * D + 8 * c)
+                        : reinterpret_cast<const u32x4*>(p.o_parts + rh * D + 8 * c);
+  const size_t o_stride = n_rh * D / (F32 ? 4 : 8);  // 16-byte units between partials
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float out_lse = -INFINITY;
   if (np <= QB) {
@@ -64,7 +76,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
       for (int i = 0; i < QB; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i], kLog2e, -m2));
       const float lse2 = m2 + __log2f(s);           // log2 of the merged sum
       out_lse = lse2 * kLn2;
-      merge_group<QB>(op, o_stride, 0, lq, lse2, acc);
+      merge_group<QB, F32>(op, o_stride, 0, lq, lse2, acc);
     }
   } else {
     float m = -INFINITY;
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
         float lq[QB];
 #pragma unroll
         for (int i = 0; i < QB; ++i) lq[i] = q0 + i < np ? lp[(q0 + i) * lse_stride] : -INFINITY;
-        merge_group<QB>(op, o_stride, q0, lq, lse2, acc);
+        merge_group<QB, F32>(op, o_stride, q0, lq, lse2, acc);
       }
     }
   }
@@ -125,8 +137,11 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream) {
   const long long blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   KernelTimer timer(KC_MERGE, stream);
-  if (d == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  const bool f32 = p.o_parts32 != nullptr;
+  if (d == 128 && f32) hipLaunchKernelGGL((merge_kernel<128, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else if (d == 128) hipLaunchKernelGGL((merge_kernel<128, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else if (f32) hipLaunchKernelGGL((merge_kernel<64, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((merge_kernel<64, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -129,6 +129,15 @@ int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
                      int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o,
                      float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Forward with O written as float32 [Tq][Hq][D] (otherwise identical to
+ * docmask_attn_fwd, same workspace): partial results for lse_merge_f32, so
+ * that a row's value is rounded to bf16 once, after the merge, instead of
+ * once per partial and again after it. */
+int docmask_attn_fwd_f32out(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                            int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
+                            int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float* o,
+                            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Backward: exact gradients of <dO, O> (FlashCP Figure 6 "Attention BWD";
  * the pages do not write it out, so this is the plain calculus):
  *   P = exp(S - LSE), Delta = rowsum(dO * O), dV = P^T dO,
@@ -154,6 +163,11 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * in float32.  Outputs must not alias inputs. */
 int lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,
               int32_t d, void* o_out, float* lse_out, hipStream_t stream);
+
+/* lse_merge over float32 partials o_parts [n_parts][rows][hq][d] (from
+ * docmask_attn_fwd_f32out); same rule, arguments and bf16 outputs. */
+int lse_merge_f32(const float* o_parts, const float* lse_parts, int32_t n_parts, int32_t rows, int32_t hq,
+                  int32_t d, void* o_out, float* lse_out, hipStream_t stream);
 
 /* Waits for `stream`, then reports device-side input errors recorded in a
  * workspace by the last call that used it: DOCMASK_OK or

@@ -164,3 +164,76 @@ def test_merge_against_oracle_small():
         want_o, want_l = oracle.lse_merge(o_b.float().numpy().astype(np.float64), lse.astype(np.float64))
         assert_close(bf16_to_np(o_m), want_o, O_TOL, "merge O")
         assert_close(l_m.cpu().numpy(), want_l, LSE_TOL, "merge LSE")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_f32_output_rounds_to_the_bf16_output(d):
+    """The float32-output forward computes the same values: rounding them to
+    bf16 (the oracle's rounding) gives the bf16 forward's bits exactly."""
+    rng = np.random.default_rng(300 + d)
+    lengths = random_lengths(rng, 900, 300, p_one=0.1)
+    w = custom_workload(77 + d, lengths, 8, 2, d, chunks=[(0, 400), (500, 400)], kv_lo=50, kv_hi=880)
+    print(f"[fwd32] d={d} lengths={lengths[:6]}", flush=True)
+    q, k, v = to_dev(w.q()), to_dev(w.k()), to_dev(w.v())
+    o16, l16 = api.attn_fwd(q, k, v, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
+    o32, l32 = api.attn_fwd(q, k, v, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale, f32_out=True)
+    torch.cuda.synchronize()
+    assert o32.dtype == torch.float32
+    assert np.array_equal(oracle.round_to_bf16_bits(o32.cpu().numpy()),
+                          o16.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert torch.equal(l16, l32)
+    want_o, want_l = oracle.attention_forward(f64(w.q()), f64(w.k()), f64(w.v()), w.cu_seqlens, w.chunks, w.kv_lo,
+                                              w.kv_hi, w.scale)
+    assert_close(o32.cpu().numpy(), want_o, O_TOL, "O32")
+
+
+def test_merge_f32_against_oracle_small():
+    rng = np.random.default_rng(5)
+    for d in (64, 128):
+        for p in (1, 5, 11):                              # 11 partials: the batched path
+            rows, hq = 77, 3
+            o = rng.standard_normal((p, rows, hq, d)).astype(np.float32)
+            lse = (3 * rng.standard_normal((p, hq, rows))).astype(np.float32)
+            lse[0, 0, :10] = -np.inf
+            lse[:, 1, 20:25] = -np.inf
+            print(f"[merge32] d={d} parts={p}", flush=True)
+            o_m, l_m = api.lse_merge(torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda())
+            torch.cuda.synchronize()
+            want_o, want_l = oracle.lse_merge(o.astype(np.float64), lse.astype(np.float64))
+            assert_close(bf16_to_np(o_m), want_o, O_TOL, "merge32 O")
+            assert_close(l_m.cpu().numpy(), want_l, LSE_TOL, "merge32 LSE")
+
+
+def test_cp_rank_f32_partials_and_merge():
+    """Rank 3 of CP = 8 with float32 partials: merged result against the
+    oracle on sampled rows, no worse than the bf16 partials' merge."""
+    w = make_config(3)
+    q, k, v = w.q(), w.k(), w.v()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    cu = w.cu_seqlens
+    need = api.schedule(cu, w.chunks, w.kv_lo, w.kv_hi, 8192, 8192)["need"].cpu().numpy()
+    row0 = 0
+    for ci, (g, n) in enumerate(w.chunks):
+        blocks = list(range(need[ci, 0] // 8192, (need[ci, 1] + 8191) // 8192))
+        print(f"[cp32] chunk {g} blocks {blocks}", flush=True)
+        p32 = torch.empty((len(blocks), n, w.hq, w.d), dtype=torch.float32, device="cuda")
+        p16 = torch.empty((len(blocks), n, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+        pl = torch.empty((len(blocks), w.hq, n), dtype=torch.float32, device="cuda")
+        for i, b in enumerate(blocks):
+            sl = slice(8192 * b, 8192 * (b + 1))
+            api.attn_fwd(qd[row0:row0 + n], kd[sl], vd[sl], cu, [(g, n)], 8192 * b, 8192 * (b + 1), w.scale,
+                         out=p32[i], lse=pl[i], f32_out=True)
+            api.attn_fwd(qd[row0:row0 + n], kd[sl], vd[sl], cu, [(g, n)], 8192 * b, 8192 * (b + 1), w.scale,
+                         out=p16[i], lse=pl[i])
+        o32, l32 = api.lse_merge(p32, pl)
+        o16, l16 = api.lse_merge(p16, pl)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([np.arange(0, n, 97), [n - 1]]))
+        want_o, want_l = oracle.attention_forward(f64(q[row0 + rows]), f64(k), f64(v), cu,
+                                                  [(g + int(r), 1) for r in rows], w.kv_lo, w.kv_hi, w.scale)
+        e32 = assert_close(bf16_to_np(o32)[rows], want_o, O_TOL, f"chunk {g} f32-partials O")
+        e16 = assert_close(bf16_to_np(o16)[rows], want_o, O_TOL, f"chunk {g} bf16-partials O")
+        assert_close(l32.cpu().numpy()[:, rows], want_l, LSE_TOL, f"chunk {g} LSE")
+        print(f"[cp32] max abs error: float32 partials {e32:.2e}, bf16 partials {e16:.2e}", flush=True)
+        assert e32 <= e16
+        row0 += n
