@@ -9,14 +9,20 @@ already resident in HBM when the timed region starts.
 `value` is useful (unmasked) attention TFLOP/s of forward + backward:
 forward 4*D*Hq*pairs, backward 10*D*Hq*pairs (five GEMM-shaped products per
 allowed pair, the QK^T recompute included); pairs = allowed (row, key) pairs
-per head.  The same run also times the forward alone, the backward alone, the
-LSE merge of one CP rank's per-block partials (2 x CP chunks 3 and 12 of
-16 x 8192, lognormal documents), and the CPU oracle on a bounded sample.
+per head.  The same run also times the forward alone and the backward alone
+(mean, and the median of 20 calls); the forward of one CP rank (rank 3 of
+CP = 8: 2 x CP chunks 3 and 12 of 16 x 8192, lognormal documents) three ways:
+per-(chunk, KV block) calls plus the LSE merge of their bf16 or float32
+partials, and one call over the rank's whole KV range; and the CPU oracle on
+a bounded sample.
+`--study sharding` instead runs the 2 x CP sharding study (every worker of
+CP = 8 under whole-sequence, per-document and Algorithm 1 plans, with their
+KV exchange).
 During the timed steps the library's event timer brackets every kernel
 launch on its stream; the roofline line is the kernel with the largest share
 of the step: its algorithmic flop per launch divided by its mean launch time.
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--study sharding]
 """
 from __future__ import annotations
 
@@ -206,6 +212,21 @@ def main():
     ms_fwd = timed(fwd, args.steps)
     ms_bwd = timed(bwd, args.steps)
     log(f"[bench] fwd {ms_fwd:.3f} ms, bwd {ms_bwd:.3f} ms")
+
+    def median_ms(fn, n=20):
+        """Median over n calls, each between its own pair of events."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    med_fwd = median_ms(fwd)
+    med_bwd = median_ms(bwd)
+    log(f"[bench] median of 20: fwd {med_fwd:.3f} ms, bwd {med_bwd:.3f} ms")
     step()                                            # leave consistent outputs behind
 
     value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
@@ -249,10 +270,14 @@ def main():
                      "launch_ms": round(dom_ms, 4)},
         "components": {
             "fwd": {"ms": round(ms_fwd, 4), "tflops": round(fwd_flop / (ms_fwd * 1e-3) / 1e12, 3),
-                    "frac_of_peak": round(fwd_flop / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                    "frac_of_peak": round(fwd_flop / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "median_of_20_ms": round(med_fwd, 4),
+                    "median_frac_of_peak": round(fwd_flop / (med_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "bwd": {"ms": round(ms_bwd, 4), "tflops": round(bwd_flop / (ms_bwd * 1e-3) / 1e12, 3),
                     "frac_of_peak": round(bwd_flop / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                    "tflops_8d_count": round(0.8 * bwd_flop / (ms_bwd * 1e-3) / 1e12, 3)},
+                    "tflops_8d_count": round(0.8 * bwd_flop / (ms_bwd * 1e-3) / 1e12, 3),
+                    "median_of_20_ms": round(med_bwd, 4),
+                    "median_frac_of_peak": round(bwd_flop / (med_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "kernels": {k: {"launches_per_step": v["launches"] // args.steps, "mean_ms": round(v["mean_ms"], 4),
                             **({"tflops": round(kernel_flop[k] / (v["mean_ms"] * 1e-3) / 1e12, 3),
                                 "frac_of_peak": round(kernel_flop[k] / (v["mean_ms"] * 1e-3) / 1e12
