@@ -91,10 +91,11 @@ def test_split_kv_backward_sums_to_full():
     assert_close(dv.cpu().numpy(), wv, O_TOL, "split dV")
 
 
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_full_size_sampled_documents(cfg):
-    w = make_config(cfg)
-    print(f"[bwd] config {cfg}: generating inputs", flush=True)
+@pytest.mark.parametrize("cfg,seed", [(4, None), (5, None), (4, 11), (4, 12), (4, 13), (5, 12)])
+def test_full_size_sampled_documents(cfg, seed):
+    """Canonical seeds (the config index) and the extra seeds 11-13."""
+    w = make_config(cfg, seed)
+    print(f"[bwd] config {cfg} seed {w.seed}: generating inputs", flush=True)
     q, k, v, do = w.q(), w.k(), w.v(), w.do()
     dq, dk, dv = _gpu_fwd_bwd(w, q, k, v, do)
     cu = w.cu_seqlens

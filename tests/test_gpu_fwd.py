@@ -108,17 +108,20 @@ def _sample_rows(w: Workload, n: int, seed: int):
     return np.unique(np.concatenate([firsts, ends, edges, rand, [0, w.tq - 1]]))
 
 
-@pytest.mark.parametrize("cfg", [2, 4, 5])
-def test_full_size_sampled_rows(cfg):
-    w = make_config(cfg)
-    _run_and_compare(w, rows=_sample_rows(w, 128 if cfg < 5 else 64, cfg), tag=f"config {cfg} sampled")
+@pytest.mark.parametrize("cfg,seed", [(2, None), (4, None), (5, None), (2, 11), (2, 12), (2, 13), (4, 11), (4, 12),
+                                      (4, 13), (5, 11)])
+def test_full_size_sampled_rows(cfg, seed):
+    """Canonical seeds (the config index) and the extra seeds 11-13."""
+    w = make_config(cfg, seed)
+    _run_and_compare(w, rows=_sample_rows(w, 128 if cfg < 5 else 64, cfg), tag=f"config {cfg} seed {w.seed} sampled")
 
 
-def test_cp_rank_partials_and_merge():
+@pytest.mark.parametrize("seed", [None, 11])
+def test_cp_rank_partials_and_merge(seed):
     """Rank 3 of CP = 8: per-chunk partials over the 8192-key blocks the need
     list names, merged with lse_merge; sampled rows vs the oracle over the full
     key range; the merged result also equals the single full-range call."""
-    w = make_config(3)
+    w = make_config(3, seed)
     q, k, v = w.q(), w.k(), w.v()
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     cu = w.cu_seqlens
