@@ -119,3 +119,31 @@ def test_full_size_sampled_documents(cfg, seed):
         assert_close(dq[t0:b][:, heads], wq, O_TOL, f"doc {doc} dQ")
         assert_close(dk[t0:b, kvh:kvh + 1], wk[t0 - a:], O_TOL, f"doc {doc} dK")
         assert_close(dv[t0:b, kvh:kvh + 1], wv[t0 - a:], O_TOL, f"doc {doc} dV")
+
+
+def test_one_million_tokens_document_tails():
+    """2^20 packed tokens: dQ/dK/dV of the last rows of the longest and the
+    last document (64-bit offsets past 2^31 bytes in dQ)."""
+    from document_masked_attention_amd.workloads import lognormal_docs
+    total = 1 << 20
+    w = custom_workload(21, lognormal_docs(21, 4096, 1.2, 64, 65536, total), 16, 2, 128, backward=True)
+    print(f"[bwd] 2^20 tokens, {len(w.lengths)} documents: generating inputs", flush=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    dq, dk, dv = _gpu_fwd_bwd(w, q, k, v, do)
+    cu = w.cu_seqlens
+    lengths = np.diff(cu)
+    g = w.hq // w.hkv
+    for doc in sorted({int(np.argmax(lengths)), len(lengths) - 1}):
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        tail = min(b - a, 128)
+        t0 = b - tail
+        kvh = doc % w.hkv
+        heads = np.arange(kvh * g, (kvh + 1) * g)
+        print(f"[bwd] 2^20 doc {doc} [{a},{b}) tail {tail} kv head {kvh}", flush=True)
+        wq, wk, wv = oracle.attention_backward(f64(q[t0:b][:, heads]), f64(k[a:b, kvh:kvh + 1]),
+                                               f64(v[a:b, kvh:kvh + 1]), f64(do[t0:b][:, heads]), cu, [(t0, tail)],
+                                               a, b, w.scale)
+        assert_close(dq[t0:b][:, heads], wq, O_TOL, f"doc {doc} dQ")
+        assert_close(dk[t0:b, kvh:kvh + 1], wk[t0 - a:], O_TOL, f"doc {doc} dK")
+        assert_close(dv[t0:b, kvh:kvh + 1], wv[t0 - a:], O_TOL, f"doc {doc} dV")
+

@@ -240,3 +240,34 @@ def test_cp_rank_f32_partials_and_merge():
         print(f"[cp32] max abs error: float32 partials {e32:.2e}, bf16 partials {e16:.2e}", flush=True)
         assert e32 <= e16
         row0 += n
+
+
+def test_max_chunks():
+    """DOCMASK_MAX_CHUNKS query chunks of 1-9 rows each over 40 documents."""
+    rng = np.random.default_rng(256)
+    lengths = [int(x) for x in rng.integers(20, 120, size=40)]
+    total = sum(lengths)
+    starts = np.sort(rng.choice(np.arange(0, total - 10, 11), size=api.MAX_CHUNKS, replace=False))
+    chunks = [(int(g), int(rng.integers(1, 10))) for g in starts]
+    w = custom_workload(256, lengths, 8, 2, 64, chunks=chunks)
+    assert len(w.chunks) == api.MAX_CHUNKS
+    _run_and_compare(w, tag="256 chunks")
+
+
+def test_one_million_tokens_sampled_rows():
+    """2^20 packed tokens (lognormal documents up to 65536): 64-bit offsets
+    past 2^31 bytes in Q and O; sampled rows against the oracle."""
+    from document_masked_attention_amd.workloads import lognormal_docs
+    total = 1 << 20
+    w = custom_workload(20, lognormal_docs(20, 4096, 1.2, 64, 65536, total), 16, 2, 128)
+    print(f"[fwd] 2^20 tokens, {len(w.lengths)} documents: generating inputs", flush=True)
+    assert w.tq * w.hq * w.d * 2 > 2 ** 31
+    q, k, v = w.q(), w.k(), w.v()
+    o, lse = api.attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.cu_seqlens, w.chunks, 0, w.total, w.scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w, 48, 20)
+    print(f"[fwd] 2^20 tokens: oracle on {rows.size} rows", flush=True)
+    want_o, want_l = oracle.attention_forward(f64(q[rows]), f64(k), f64(v), w.cu_seqlens,
+                                              [(int(r), 1) for r in rows], 0, w.total, w.scale)
+    assert_close(bf16_to_np(o[torch.as_tensor(rows, device="cuda")]), want_o, O_TOL, "2^20 O")
+    assert_close(lse[:, torch.as_tensor(rows, device="cuda")].cpu().numpy(), want_l, LSE_TOL, "2^20 LSE")
