@@ -85,6 +85,29 @@ def read_traffic(kernel: str):
         return None
 
 
+MERGE_PMC = "merge_kernel_cp8_rank3_T131072_lognormal2048_h32x8_d128_pmc.txt"
+
+
+def read_merge_traffic(key: str):
+    """HBM bytes per merge pass (`merge_kernel` or `merge_kernel_f32`) from the
+    committed counter summary, or None if absent or taken on other source."""
+    path = os.path.join(PROFILE_DIR, MERGE_PMC)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(["merge.hip", "common.h", "kernels.h"]):
+        return None
+    try:
+        return float(vals[f"{key}.hbm_bytes_per_pass"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, min_tokens: int = 14000):
     """The oracle, as it stands, on whole documents covering the first
     `min_tokens` tokens of the workload, one KV-head group (fwd + bwd)."""
@@ -450,11 +473,12 @@ def bench_merge(api, torch, dev, upload, steps):
         "fwd_kernel_ms": round(f32_fwd_ms, 4), "merge_ms": round(f32_merge_ms, 4),
         "total_ms": round(f32_fwd_ms + f32_merge_ms, 4), "merge_bytes": int(bytes32),
         "merge_GBps": round(bytes32 / (f32_merge_ms * 1e-3) / 1e9, 1),
+        "merge_traffic": read_merge_traffic("merge_kernel_f32"),
         "note": "per-block forward calls writing float32 O, then lse_merge_f32 (bf16 output)"}})
     del jobs32
     merge = {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
              "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-             "bound": "hbm"}
+             "bound": "hbm", "traffic": read_merge_traffic("merge_kernel")}
     return merge, cp_fwd
 
 
