@@ -509,7 +509,7 @@ def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps)
         slot = max([n for _, n in send] + [1])
         gk = torch.zeros((cp * slot, hkv, d), dtype=torch.bfloat16, device=dev)
         gv = torch.zeros_like(gk)
-        pack_ms, unpack_ms, pack_bytes, unpack_bytes = [], [], [], []
+        pack_ms, unpack_ms, pack_bytes, unpack_bytes, written_rows, span_rows = [], [], [], [], [], []
         locs = []
         for r, ch in enumerate(plan):
             pos = torch.as_tensor(np.concatenate([np.arange(g, g + n) for g, n in ch]), device=dev)
@@ -537,7 +537,7 @@ def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps)
             kl, vl = locs[r]
 
             def place():
-                api.copy_rows(gk, gv, bk, bv, m["remote"], True)
+                api.copy_rows(gk, gv, bk, bv, m["remote"], False)
                 api.copy_rows(kl, vl, bk, bv, m["local"], False)
             place()
             torch.cuda.synchronize()
@@ -547,9 +547,12 @@ def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps)
             torch.cuda.synchronize()
             unpack_ms.append(api.timing_read(api.KERNEL_COPY)[0] / reps)
             api.timing_enable(False)
-            remote_rows = sum(x[2] for x in m["remote"])
+            copied = sum(x[2] for x in m["remote"] if x[0] >= 0)
+            zeros = sum(x[2] for x in m["remote"] if x[0] < 0)
             own = sum(x[2] for x in m["local"])
-            unpack_bytes.append(2 * rb * (remote_rows + span + 2 * own))
+            unpack_bytes.append(2 * rb * (2 * copied + zeros + 2 * own))
+            written_rows.append(copied + zeros + own)
+            span_rows.append(span)
             del bk, bv
         sent = [n for _, n in send]
         eq4 = 4.0 * total / cp * hkv * d * (cp - 1) * 2
@@ -562,8 +565,9 @@ def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps)
             "pack_GBps": round(float(pb.sum() / (pm.sum() * 1e-3) / 1e9), 1) if pm.sum() > 0 else None,
             "unpack_GBps": round(float(ub.sum() / (um.sum() * 1e-3) / 1e9), 1),
             "unpack_frac_of_hbm_peak": round(float(ub.sum() / (um.sum() * 1e-3) / 1e9 / PEAK_HBM_GBS), 4),
-            "bytes_note": "pack: K and V sent rows read + written; place: gathered rows read, the whole KV range "
-                          "written (zeros between), own rows read + written"}
+            "placed_rows_written": int(sum(written_rows)), "placed_range_rows": int(sum(span_rows)),
+            "bytes_note": "pack: K and V sent rows read + written; place: gathered and own rows read + written, "
+                          "zero rows written (the rest of each 128-row KV block holding a needed row)"}
         log(f"[study] exchange {sharding}: eq5/eq4 {eq5 / eq4:.3f}, pack {out[sharding]['pack_GBps']} GB/s, "
             f"place {out[sharding]['unpack_GBps']} GB/s")
         del gk, gv, locs

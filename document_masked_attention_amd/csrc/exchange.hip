@@ -14,9 +14,15 @@
 // copy_rows_kernel streams 16-byte units; each workgroup takes a contiguous
 // span of destination units, finds the first map that reaches it (binary
 // search over the map table in LDS), and every thread walks the maps forward
-// as its units advance.  Gap rows (covered by no map) are zeroed or left
-// alone.  Bandwidth bound: covered rows are read once, every written row is
-// written once.
+// as its units advance.  A map with source -1 writes zero rows; gap rows
+// (covered by no map) are zeroed or left alone.  Bandwidth bound: copied rows
+// are read once, every written row is written once.
+//
+// The attention kernels read KV in whole tiles of at most kZeroBlock rows
+// counted from kv_lo, and give keys outside a query's document weight zero,
+// so the placement writes zeros over the rows of those tiles that no chunk
+// needs (finite values for the masked keys) and leaves the rest of the range
+// untouched.
 #include "docmask.h"
 #include "kernels.h"
 
@@ -35,7 +41,7 @@ struct CopyTable {
   int32_t n;
   int32_t dst_lo[kCopyMaps];        // destination rows [dst_lo, dst_hi), relative to the launch's first row
   int32_t dst_hi[kCopyMaps];
-  int32_t src[kCopyMaps];           // source row of dst_lo
+  int32_t src[kCopyMaps];           // source row of dst_lo; -1: zero rows
 };
 
 struct CopyParams {
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(CopyParams p, C
       const bool covered = valid && i < n && (int64_t)s_lo[i] * ru <= u;
       a[k] = u32x4{0u, 0u, 0u, 0u};
       b[k] = u32x4{0u, 0u, 0u, 0u};
-      if (covered) {
+      if (covered && s_src[i] >= 0) {                 // src -1: a run of zero rows
         const int64_t s = (int64_t)s_src[i] * ru + (u - (int64_t)s_lo[i] * ru);
         a[k] = __builtin_nontemporal_load(p.src_k + s);
         if (two) b[k] = __builtin_nontemporal_load(p.src_v + s);
@@ -149,6 +155,8 @@ hipError_t launch_copy_rows(const void* src_k, const void* src_v, void* dst_k, v
 namespace {
 
 using docmask::launch_copy_rows;
+
+constexpr int32_t kZeroBlock = 128;   // largest KV tile of the attention kernels (rows from kv_lo)
 
 struct Piece {
   int32_t g;       // global start
@@ -228,18 +236,23 @@ int docmask_copy_rows(const void* src_k, const void* src_v, int64_t src_rows, vo
   std::vector<docmask_rowmap> m;
   m.reserve(n_maps);
   int64_t prev_end = 0;
+  bool reads = false;
   for (int32_t i = 0; i < n_maps; ++i) {
     const docmask_rowmap r = maps[i];
-    if (r.len < 0 || r.src < 0 || r.dst < prev_end) return DOCMASK_EINVAL;
-    if ((int64_t)r.src + r.len > src_rows || (int64_t)r.dst + r.len > dst_rows) return DOCMASK_EINVAL;
+    if (r.len < 0 || r.src < -1 || r.dst < prev_end) return DOCMASK_EINVAL;
+    if ((r.src >= 0 && (int64_t)r.src + r.len > src_rows) || (int64_t)r.dst + r.len > dst_rows)
+      return DOCMASK_EINVAL;
     prev_end = (int64_t)r.dst + r.len;
-    if (r.len > 0) m.push_back(r);
+    if (r.len > 0) {
+      m.push_back(r);
+      reads = reads || r.src >= 0;
+    }
   }
   const bool writes = dst_rows > 0 && (!m.empty() || zero_gaps);
   if (!writes) return DOCMASK_OK;                 // empty tensors may come with null pointers
-  if ((src_v == nullptr) != (dst_v == nullptr) && !(m.empty() && src_v == nullptr)) return DOCMASK_EINVAL;
+  if ((src_v == nullptr) != (dst_v == nullptr) && !(!reads && src_v == nullptr)) return DOCMASK_EINVAL;
   if (!dst_k || !aligned16(dst_k) || (dst_v && !aligned16(dst_v))) return DOCMASK_EINVAL;
-  if (!m.empty() && (!src_k || !aligned16(src_k) || (src_v && !aligned16(src_v)))) return DOCMASK_EINVAL;
+  if (reads && (!src_k || !aligned16(src_k) || (src_v && !aligned16(src_v)))) return DOCMASK_EINVAL;
   const hipError_t e = launch_copy_rows(src_k, src_v, dst_k, dst_v, dst_rows, row_bytes, m.data(),
                                         (int32_t)m.size(), zero_gaps != 0, stream);
   return e == hipSuccess ? DOCMASK_OK : DOCMASK_EHIP;
@@ -324,6 +337,34 @@ int docmask_exchange_recv_maps(const int32_t* cu_seqlens, int32_t n_docs, const 
         }
       }
       packed += pc.len;
+    }
+  }
+  // zero runs: rows of the kZeroBlock-row blocks (from kv_lo) that meet a need
+  // interval and that neither another worker's rows nor this worker's own fill
+  {
+    std::vector<std::pair<int64_t, int64_t>> held;             // destination rows written by copies
+    for (const docmask_rowmap& r : rem) held.emplace_back(r.dst, (int64_t)r.dst + r.len);
+    for (int32_t c = 0; c < n_mine; ++c)
+      if (mine[c].len > 0) held.emplace_back(mine[c].g_start - *kv_lo, (int64_t)mine[c].g_start - *kv_lo + mine[c].len);
+    std::sort(held.begin(), held.end());
+    const int64_t span = (int64_t)*kv_hi - *kv_lo;
+    std::vector<std::pair<int64_t, int64_t>> blocks;
+    for (const auto& nd : need) {
+      const int64_t a = (nd.first - *kv_lo) / kZeroBlock * kZeroBlock;
+      const int64_t b = std::min<int64_t>(((int64_t)nd.second - *kv_lo + kZeroBlock - 1) / kZeroBlock * kZeroBlock, span);
+      if (!blocks.empty() && a <= blocks.back().second) blocks.back().second = std::max(blocks.back().second, b);
+      else blocks.emplace_back(a, b);
+    }
+    size_t hi_i = 0;
+    for (const auto& bl : blocks) {
+      int64_t pos = bl.first;
+      while (hi_i < held.size() && held[hi_i].second <= pos) ++hi_i;
+      for (size_t t = hi_i; pos < bl.second; ++t) {
+        const int64_t next = t < held.size() ? std::min(held[t].first, bl.second) : bl.second;
+        if (next > pos) rem.push_back(docmask_rowmap{-1, (int32_t)pos, (int32_t)(next - pos)});
+        if (t >= held.size()) break;
+        pos = std::max(pos, held[t].second);
+      }
     }
   }
   std::sort(rem.begin(), rem.end(), [](const docmask_rowmap& x, const docmask_rowmap& y) { return x.dst < y.dst; });

@@ -204,14 +204,16 @@ typedef struct {
 
 /* Copies rows by a map list: dst[m.dst + t] = src[m.src + t] for every map m
  * and t < m.len, for one tensor (src_v = dst_v = NULL) or two (K and V, same
- * maps).  Rows are row_bytes long (a positive multiple of 16; Hkv * D * 2 for
- * bf16 KV).  Maps must be sorted by dst and disjoint there, with len >= 0 and
+ * maps); a map with src = -1 writes len zero rows at dst instead.  Rows are
+ * row_bytes long (a positive multiple of 16; Hkv * D * 2 for bf16 KV).  Maps
+ * must be sorted by dst and disjoint there, with len >= 0, src >= -1 and
  * every row inside [0, src_rows) and [0, dst_rows); any number of maps (one
  * launch per 128).  zero_gaps != 0 also zeroes every destination row that no
  * map covers, so that the whole of [0, dst_rows) is written; otherwise those
  * rows are left untouched.  Source and destination must not overlap; tensor
- * pointers 16-byte aligned; a call that writes nothing (dst_rows = 0, or no
- * map and no zeroing) checks no pointer.  Bandwidth bound: covered rows are read once and
+ * pointers 16-byte aligned; source pointers are checked only when a map
+ * copies, and a call that writes nothing (dst_rows = 0, or no map and no
+ * zeroing) checks no pointer.  Bandwidth bound: copied rows are read once and
  * every written row is written once. */
 int docmask_copy_rows(const void* src_k, const void* src_v, int64_t src_rows, void* dst_k, void* dst_v,
                       int64_t dst_rows, int64_t row_bytes, const docmask_rowmap* maps, int32_t n_maps,
@@ -258,10 +260,13 @@ int docmask_exchange_send_maps(const int32_t* cu_seqlens, int32_t n_docs, const 
  * chunk's first row up to the chunk end; 0, 0 without rows); `remote` = maps
  * from the gathered buffer to rows of [kv_lo, kv_hi) (position - kv_lo),
  * covering exactly the other workers' sent rows inside the need intervals,
- * sorted by dst; `local` = maps from the worker's local KV rows to the same
- * destination (one per non-empty chunk).  Copying `remote` with zero_gaps and
- * then `local` without fills [kv_lo, kv_hi) with every row an allowed pair
- * can reach and zeros elsewhere.  NULL map arrays only report counts;
+ * plus zero runs (src = -1), sorted by dst; `local` = maps from the worker's
+ * local KV rows to the same destination (one per non-empty chunk).  Copying
+ * `remote` and `local` (no zero_gaps) writes every row an allowed pair can
+ * reach, and zeros over the other rows of each 128-row block (counted from
+ * kv_lo) that holds such a row: the attention entry points read KV in whole
+ * tiles of at most 128 rows from kv_lo, so the rest of [kv_lo, kv_hi) is
+ * never read and stays untouched.  NULL map arrays only report counts;
  * capacities below the counts are DOCMASK_EINVAL. */
 int docmask_exchange_recv_maps(const int32_t* cu_seqlens, int32_t n_docs, const docmask_chunk* all_chunks,
                                const int32_t* rank_n_chunks, int32_t n_ranks, int32_t rank, int64_t slot_rows,

@@ -128,7 +128,8 @@ def test_copy_rows_validation(lib):
     assert _copy(lib, maps=((0, 0, 4), (0, 3, 2))) == api.EINVAL        # overlapping destinations
     assert _copy(lib, maps=((8, 0, 4),)) == api.EINVAL                  # source past its end
     assert _copy(lib, maps=((0, 8, 4),)) == api.EINVAL                  # destination past its end
-    assert _copy(lib, maps=((-1, 0, 4),)) == api.EINVAL
+    assert _copy(lib, maps=((-2, 0, 4),)) == api.EINVAL                 # -1 is the only negative source (zeros)
+    assert _copy(lib, maps=((-1, 8, 4),)) == api.EINVAL                 # zero run past the destination end
     assert _copy(lib, maps=((0, 0, -1),)) == api.EINVAL
     assert _copy(lib, src_v=None) == api.EINVAL                         # K and V must come together
     assert _copy(lib, dst_k=MIS) == api.EINVAL

@@ -1,19 +1,22 @@
 """Host-side exchange planning of the library (send and receive row maps)
 against the oracle, on the CPU: the maps are applied with numpy slicing here,
-so this checks which rows travel and where they land; the GPU copy of the
-same maps is checked in test_gpu_exchange.py."""
+so this checks which rows travel and where they land (needed rows from the
+oracle; zeros over the rest of each 128-row block that holds one, nothing
+written elsewhere); the GPU copy of the same maps is checked in
+test_gpu_exchange.py."""
 import numpy as np
 import pytest
 
 import oracle
 from document_masked_attention_amd import api
+from placement_util import check_placement
 from document_masked_attention_amd.workloads import (cu_from_lengths, per_doc_chunks, sequence_zigzag_chunks,
                                                      random_plan, lognormal_docs)
 
 
 def _apply(maps, src, dst):
     for s, d, n in maps:
-        dst[d:d + n] = src[s:s + n]
+        dst[d:d + n] = 0 if s == -1 else src[s:s + n]
     return dst
 
 
@@ -66,9 +69,10 @@ def test_maps_against_oracle(case):
         assert (m["kv_lo"], m["kv_hi"]) == (lo, hi)
         dsts = [d for _, d, _ in m["remote"]]
         assert dsts == sorted(dsts)
-        buf = _apply(m["remote"], gathered, np.zeros((hi - lo, 3), kv.dtype))    # zero_gaps
+        buf = _apply(m["remote"], gathered, np.full((hi - lo, 3), -1, kv.dtype))
         buf = _apply(m["local"], kv[oracle.local_positions(chunks)], buf)
-        assert np.array_equal(buf, want), f"rank {r}"
+        need = oracle.needed_positions(cu, chunks, total)[lo:hi]
+        check_placement(buf, want, need, -1, f"rank {r}")
 
 
 def test_planning_rejects_bad_plans():

@@ -1,7 +1,8 @@
 """KV exchange on the GPU: the row-copy kernel against numpy slicing, and the
 whole single-GPU side of the sharding-aware exchange (pack the rows a worker
 sends, place gathered rows at their positions) against the oracle, bit for
-bit, followed by attention over the placed KV against the oracle."""
+bit, followed by forward and backward over the placed KV against the oracle,
+with every row the placement leaves untouched holding NaN."""
 import numpy as np
 import pytest
 import torch
@@ -11,17 +12,22 @@ from document_masked_attention_amd import api
 from document_masked_attention_amd.workloads import (custom_workload, per_doc_chunks, random_plan, fig3_workload,
                                                      sequence_zigzag_chunks, draw_tensor)
 from gpu_util import to_dev, bf16_to_np, f64, assert_close, O_TOL, LSE_TOL
+from placement_util import check_placement
 
 pytestmark = pytest.mark.gpu
 
+NAN_BITS = 0x7FC0          # bf16 quiet NaN
+
 
 def _random_maps(rng, src_rows, dst_rows, n):
+    """Disjoint ascending destination runs; about one in five writes zeros (source -1)."""
     pts = np.sort(rng.choice(dst_rows + 1, size=min(2 * n, dst_rows + 1), replace=False))
     maps = []
     for j in range(0, len(pts) - 1, 2):
         d, e = int(pts[j]), int(pts[j + 1])
         length = min(e - d, src_rows)
-        maps.append((int(rng.integers(0, src_rows - length + 1)), d, length))
+        src = -1 if rng.random() < 0.2 else int(rng.integers(0, src_rows - length + 1))
+        maps.append((src, d, length))
     return maps
 
 
@@ -46,7 +52,7 @@ def test_copy_rows_random(row_bytes):
             want = np.full((dst_rows, w), 0 if zero else fill, dtype=np.int32)
             s_np = src.cpu().numpy()
             for s, d, n in maps:
-                want[d:d + n] = s_np[s:s + n]
+                want[d:d + n] = 0 if s == -1 else s_np[s:s + n]
             assert np.array_equal(dst.cpu().numpy(), want)
 
 
@@ -97,15 +103,18 @@ def _exchange(plan, lengths, hkv, d, seed):
     for r, chunks in enumerate(plan):
         m = api.exchange_recv_maps(cu, plan, r, slot)
         lo, hi = m["kv_lo"], m["kv_hi"]
-        bk = torch.empty((hi - lo, hkv, d), dtype=torch.bfloat16, device="cuda")
-        bv = torch.empty_like(bk)
-        api.copy_rows(gk, gv, bk, bv, m["remote"], True)
+        # rows the placement must not write hold NaN: attention over the
+        # placed KV then proves that no kernel reads them
+        bk = torch.full((hi - lo, hkv, d), NAN_BITS, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        bv = torch.full((hi - lo, hkv, d), NAN_BITS, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        api.copy_rows(gk, gv, bk, bv, m["remote"], False)
         api.copy_rows(packed[r][2], packed[r][3], bk, bv, m["local"], False)
         torch.cuda.synchronize()
+        need = oracle.needed_positions(cu, chunks, total)[lo:hi]
         for buf, glob in ((bk, kg), (bv, vg)):
             wlo, whi, want = oracle.received_kv(glob, cu, chunks)
             assert (wlo, whi) == (lo, hi)
-            assert np.array_equal(buf.view(torch.int16).cpu().numpy().view(np.uint16), want), f"rank {r}"
+            check_placement(buf.view(torch.int16).cpu().numpy().view(np.uint16), want, need, NAN_BITS, f"rank {r}")
         out.append((chunks, lo, hi, bk, bv))
     return cu, out
 
@@ -135,13 +144,19 @@ def test_exchange_then_attention_small(kind):
         if not chunks:
             continue
         w = custom_workload(seed, lengths, hq, hkv, d, chunks=chunks)
-        q = w.q()
-        o, lse = api.attn_fwd(to_dev(q), bk, bv, cu, chunks, lo, hi, w.scale)
+        q, do = w.q(), w.do()
+        qd, dod = to_dev(q), to_dev(do)
+        o, lse = api.attn_fwd(qd, bk, bv, cu, chunks, lo, hi, w.scale)
+        dq, dk, dv = api.attn_bwd(qd, bk, bv, o, lse, dod, cu, chunks, lo, hi, w.scale)
         torch.cuda.synchronize()
         kg, vg = draw_tensor(seed, "k", w.total, hkv, d), draw_tensor(seed, "v", w.total, hkv, d)
         want_o, want_l = oracle.attention_forward(f64(q), f64(kg), f64(vg), cu, chunks, 0, w.total, w.scale)
         assert_close(bf16_to_np(o), want_o, O_TOL, f"rank {r} O")
         assert_close(lse.cpu().numpy(), want_l, LSE_TOL, f"rank {r} LSE")
+        wq, wk, wv = oracle.attention_backward(f64(q), f64(kg), f64(vg), f64(do), cu, chunks, 0, w.total, w.scale)
+        assert_close(dq.cpu().numpy(), wq, O_TOL, f"rank {r} dQ")
+        assert_close(dk.cpu().numpy(), wk[lo:hi], O_TOL, f"rank {r} dK")
+        assert_close(dv.cpu().numpy(), wv[lo:hi], O_TOL, f"rank {r} dV")
 
 
 def test_exchange_study_plan_full_size():
