@@ -314,8 +314,8 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_merge:
-        result["components"]["merge"], result["components"]["cp_rank_forward"] = bench_merge(
-            api, torch, dev, upload, args.steps)
+        (result["components"]["merge"], result["components"]["cp_rank_forward"],
+         result["components"]["cp_rank_backward"]) = bench_merge(api, torch, dev, upload, args.steps)
     if args.copy_calibration:
         # a streaming kernel of known size for scaling HBM byte counters: the
         # library's f32 -> bf16 conversion reads 1 GiB and writes 512 MiB
@@ -476,10 +476,55 @@ def bench_merge(api, torch, dev, upload, steps):
         "merge_traffic": read_merge_traffic("merge_kernel_f32"),
         "note": "per-block forward calls writing float32 O, then lse_merge_f32 (bf16 output)"}})
     del jobs32
+    # the rank's backward as a ring schedule runs it: per-(chunk, KV block)
+    # calls with the merged O and LSE (dQ shares accumulated, Delta formed by
+    # the first call of each chunk), beside one call over the whole KV range
+    merge_all()
+    do_r = upload(w.do())
+    dq_r = torch.empty((w.tq, w.hq, w.d), dtype=torch.float32, device=dev)
+    dk_b = torch.empty((blk, w.hkv, w.d), dtype=torch.float32, device=dev)
+    dv_b = torch.empty_like(dk_b)
+    ws_c = {}
+    for r0, g, n, blocks, _, _ in fwd_calls:
+        ws_c[g] = torch.empty(max(api.workspace_size(api.OP_BWD, len(w.lengths), [(g, n)], blk * b, blk * (b + 1),
+                                                     w.hq, w.hkv, w.d) for b in blocks), dtype=torch.uint8, device=dev)
+
+    def bwd_all():
+        for (r0, g, n, blocks, _, _), (_, _, oo, lo) in zip(fwd_calls, jobs):
+            for i, b in enumerate(blocks):
+                api.attn_bwd(q[r0:r0 + n], k[blk * b:blk * (b + 1)], v[blk * b:blk * (b + 1)], oo, lo,
+                             do_r[r0:r0 + n], cu, [(g, n)], blk * b, blk * (b + 1), w.scale, dq=dq_r[r0:r0 + n],
+                             dk=dk_b, dv=dv_b, accumulate_dq=i > 0, delta_ready=i > 0, workspace=ws_c[g])
+
+    dq1 = torch.empty((w.tq, w.hq, w.d), dtype=torch.float32, device=dev)
+    dk1 = torch.empty((w.tkv, w.hkv, w.d), dtype=torch.float32, device=dev)
+    dv1 = torch.empty_like(dk1)
+
+    def bwd_one():
+        api.attn_bwd(q, k, v, o1, l1, do_r, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale, dq=dq1, dk=dk1, dv=dv1)
+
+    bwd_flop = 10.0 * w.d * w.hq * pairs
+    legs = {}
+    for name, fn in (("per_block", bwd_all), ("single_call", bwd_one)):
+        fn()
+        torch.cuda.synchronize()
+        api.timing_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        kms = sum(api.timing_read(c)[0] for c in (api.KERNEL_SCHEDULE, api.KERNEL_DQ, api.KERNEL_DKDV)) / reps
+        calls = api.timing_read(api.KERNEL_DKDV)[1] // reps
+        api.timing_enable(False)
+        legs[name] = {"kernel_ms": round(kms, 4), "calls_per_pass": calls,
+                      "tflops": round(bwd_flop / (kms * 1e-3) / 1e12, 2),
+                      "frac_of_peak": round(bwd_flop / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    cp_bwd = {"workload": w.name, "useful_tflop": round(bwd_flop / 1e12, 3), **legs,
+              "note": "scheduler + dQ + dK/dV kernel time; useful work 10*D*Hq*pairs"}
+    del do_r, dq_r, dk_b, dv_b, dq1, dk1, dv1, ws_c
     merge = {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
              "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
              "bound": "hbm", "traffic": read_merge_traffic("merge_kernel")}
-    return merge, cp_fwd
+    return merge, cp_fwd, cp_bwd
 
 
 FLASHCP_RATIO = 1.05         # target workload ratio of the planner in the sharding study

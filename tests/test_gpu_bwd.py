@@ -147,3 +147,51 @@ def test_one_million_tokens_document_tails():
         assert_close(dk[t0:b, kvh:kvh + 1], wk[t0 - a:], O_TOL, f"doc {doc} dK")
         assert_close(dv[t0:b, kvh:kvh + 1], wv[t0 - a:], O_TOL, f"doc {doc} dV")
 
+
+
+def test_cp_rank_split_backward():
+    """Rank 3 of CP = 8 run as a ring rank runs it: per-(chunk, 8192-key block)
+    backward calls with the merged O and LSE, dQ shares accumulated, Delta
+    formed by each chunk's first call; equals the single call over the whole
+    KV range, whose dQ on sampled rows matches the oracle."""
+    w = make_config(3)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    cu = w.cu_seqlens
+    o1, l1 = api.attn_fwd(qd, kd, vd, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale)
+    dq1, dk1, dv1 = api.attn_bwd(qd, kd, vd, o1, l1, dod, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale)
+    need = api.schedule(cu, w.chunks, w.kv_lo, w.kv_hi, 8192, 8192)["need"].cpu().numpy()
+    dq = torch.empty_like(dq1)
+    dk = torch.zeros_like(dk1)
+    dv = torch.zeros_like(dv1)
+    row0 = 0
+    for ci, (g, n) in enumerate(w.chunks):
+        blocks = list(range(need[ci, 0] // 8192, (need[ci, 1] + 8191) // 8192))
+        print(f"[cp bwd] chunk {g} blocks {blocks}", flush=True)
+        rows = slice(row0, row0 + n)
+        po = torch.empty((len(blocks), n, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+        pl = torch.empty((len(blocks), w.hq, n), dtype=torch.float32, device="cuda")
+        for i, b in enumerate(blocks):
+            sl = slice(8192 * b, 8192 * (b + 1))
+            api.attn_fwd(qd[rows], kd[sl], vd[sl], cu, [(g, n)], sl.start, sl.stop, w.scale, out=po[i], lse=pl[i])
+        om, lm = api.lse_merge(po, pl)
+        ws = torch.empty(api.workspace_size(api.OP_BWD, len(w.lengths), [(g, n)], 0, 8192, w.hq, w.hkv, w.d),
+                         dtype=torch.uint8, device="cuda")
+        dkb = torch.empty((8192, w.hkv, w.d), dtype=torch.float32, device="cuda")
+        dvb = torch.empty_like(dkb)
+        for i, b in enumerate(blocks):
+            sl = slice(8192 * b, 8192 * (b + 1))
+            api.attn_bwd(qd[rows], kd[sl], vd[sl], om, lm, dod[rows], cu, [(g, n)], sl.start, sl.stop, w.scale,
+                         dq=dq[rows], dk=dkb, dv=dvb, accumulate_dq=i > 0, delta_ready=i > 0, workspace=ws)
+            dk[sl] += dkb
+            dv[sl] += dvb
+        row0 += n
+    torch.cuda.synchronize()
+    assert_close(dq.cpu().numpy(), dq1.cpu().numpy(), O_TOL, "per-block vs single-call dQ")
+    assert_close(dk.cpu().numpy(), dk1.cpu().numpy(), O_TOL, "per-block vs single-call dK")
+    assert_close(dv.cpu().numpy(), dv1.cpu().numpy(), O_TOL, "per-block vs single-call dV")
+    sel = np.unique(np.concatenate([np.arange(0, w.tq, 1021), [w.tq - 1]]))
+    pos = w.local_positions()
+    wq, _, _ = oracle.attention_backward(f64(q[sel]), f64(k), f64(v), f64(do[sel]), cu,
+                                         [(int(pos[r]), 1) for r in sel], w.kv_lo, w.kv_hi, w.scale)
+    assert_close(dq1.cpu().numpy()[sel], wq, O_TOL, "single-call dQ vs oracle")
