@@ -13,8 +13,8 @@ per head.  The same run also times the forward alone and the backward alone
 (mean, and the median of 20 calls); the forward of one CP rank (rank 3 of
 CP = 8: 2 x CP chunks 3 and 12 of 16 x 8192, lognormal documents) three ways:
 per-(chunk, KV block) calls plus the LSE merge of their bf16 or float32
-partials, and one call over the rank's whole KV range; and the CPU oracle on
-a bounded sample.
+partials, and one call over the rank's whole KV range, and its backward the
+same two ways; and the CPU oracle on a bounded sample.
 `--study sharding` instead runs the 2 x CP sharding study (every worker of
 CP = 8 under whole-sequence, per-document and Algorithm 1 plans, with their
 KV exchange).
