@@ -22,7 +22,7 @@ During the timed steps the library's event timer brackets every kernel
 launch on its stream; the roofline line is the kernel with the largest share
 of the step: its algorithmic flop per launch divided by its mean launch time.
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--study sharding]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--study sharding|length]
 """
 from __future__ import annotations
 
@@ -147,9 +147,10 @@ def main():
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the f32->bf16 conversion over 1 GiB (reference for HBM byte counters)")
-    ap.add_argument("--study", choices=["sharding"],
-                    help="instead of the step benchmark, time every CP rank's forward under per-sequence and "
-                         "per-document 2 x CP sharding (1 x 131072, 16 x 8192 and bimodal documents)")
+    ap.add_argument("--study", choices=["sharding", "length"],
+                    help="instead of the step benchmark: 'sharding' times every CP rank's forward under "
+                         "per-sequence, per-document and Algorithm 1 sharding; 'length' times forward and "
+                         "backward of one GPU's sequence from 32K to 1M tokens")
     ap.add_argument("--cp", type=int, default=8, help="CP size of the sharding study")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -158,6 +159,9 @@ def main():
         sys.exit(2)
     if args.study == "sharding":
         study_sharding(args.cp, max(args.steps, 3))
+        return
+    if args.study == "length":
+        study_length(max(args.steps, 3))
         return
 
     import torch
@@ -617,6 +621,61 @@ def exchange_study(api, torch, dev, kf, vf, lengths, cp, hq, hkv, d, seed, reps)
             f"place {out[sharding]['unpack_GBps']} GB/s")
         del gk, gv, locs
     return out
+
+
+def study_length(reps: int):
+    """Forward and backward of one GPU's packed sequence at 32K to 1M tokens
+    (lognormal(2048, 1.5) documents up to 131072 tokens, 32 query / 8 KV heads,
+    D = 128): kernel time by the library's event timer, useful TFLOP/s and the
+    fraction of dense bf16 peak at each length."""
+    import torch
+    from document_masked_attention_amd import api
+    from document_masked_attention_amd.workloads import custom_workload, lognormal_docs
+    api.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hq, hkv, d = 32, 8, 128
+    out = {"study": "sequence length", "q_heads": hq, "kv_heads": hkv, "head_dim": d, "reps": reps,
+           "documents": "lognormal(2048, 1.5), clip [64, 131072], seed 9", "lengths": []}
+
+    def dev_bits(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    for t in (1 << 15, 1 << 17, 1 << 19, 1 << 20):
+        w = custom_workload(9, lognormal_docs(9, 2048, 1.5, 64, 131072, t), hq, hkv, d, backward=True)
+        log(f"[study] length {t}: {len(w.lengths)} documents, generating inputs")
+        q, k, v, do = dev_bits(w.q()), dev_bits(w.k()), dev_bits(w.v()), dev_bits(w.do())
+        cu = torch.as_tensor(w.cu_seqlens, dtype=torch.int32, device=dev)
+        pairs = int(api.schedule(cu, w.chunks, 0, t, 128, 64)["counters"][3].item())
+        o, lse = api.attn_fwd(q, k, v, cu, w.chunks, 0, t, w.scale)
+        dq, dk, dv = api.attn_bwd(q, k, v, o, lse, do, cu, w.chunks, 0, t, w.scale)
+        torch.cuda.synchronize()
+        api.timing_enable(True)
+        for _ in range(reps):
+            api.attn_fwd(q, k, v, cu, w.chunks, 0, t, w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        fwd_ms = (api.timing_read(api.KERNEL_FWD)[0] + api.timing_read(api.KERNEL_SCHEDULE)[0]) / reps
+        api.timing_enable(False)
+        api.timing_enable(True)
+        for _ in range(reps):
+            api.attn_bwd(q, k, v, o, lse, do, cu, w.chunks, 0, t, w.scale, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        bwd_ms = sum(api.timing_read(c)[0] for c in (api.KERNEL_SCHEDULE, api.KERNEL_DQ, api.KERNEL_DKDV)) / reps
+        api.timing_enable(False)
+        ff, bf = 4.0 * d * hq * pairs, 10.0 * d * hq * pairs
+        row = {"tokens": t, "documents": len(w.lengths), "pairs_per_head": pairs,
+               "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 1),
+               "fwd_frac_of_peak": round(ff / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "bwd_ms": round(bwd_ms, 4), "bwd_tflops": round(bf / (bwd_ms * 1e-3) / 1e12, 1),
+               "bwd_frac_of_peak": round(bf / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "resident_gib": round(sum(x.numel() * x.element_size() for x in (q, k, v, do, o, lse, dq, dk, dv))
+                                     / 2 ** 30, 2)}
+        out["lengths"].append(row)
+        log(f"[study] length {t}: fwd {fwd_ms:.3f} ms ({row['fwd_frac_of_peak']:.3f}), "
+            f"bwd {bwd_ms:.3f} ms ({row['bwd_frac_of_peak']:.3f})")
+        del q, k, v, do, o, lse, dq, dk, dv
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
 
 
 def study_sharding(cp: int, reps: int):
