@@ -13,8 +13,8 @@ per head.  The same run also times the forward alone and the backward alone
 (mean, and the median of 20 calls); the forward of one CP rank (rank 3 of
 CP = 8: 2 x CP chunks 3 and 12 of 16 x 8192, lognormal documents) three ways:
 per-(chunk, KV block) calls plus the LSE merge of their bf16 or float32
-partials, and one call over the rank's whole KV range, and its backward the
-same two ways; and the CPU oracle on a bounded sample.
+partials, and one call over the rank's whole KV range (with --cp-backward
+also its backward the same two ways); and the CPU oracle on a bounded sample.
 `--study sharding` instead runs the 2 x CP sharding study (every worker of
 CP = 8 under whole-sequence, per-document and Algorithm 1 plans, with their
 KV exchange).
@@ -22,7 +22,7 @@ During the timed steps the library's event timer brackets every kernel
 launch on its stream; the roofline line is the kernel with the largest share
 of the step: its algorithmic flop per launch divided by its mean launch time.
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--study sharding|length]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--cp-backward] [--study sharding|length]
 """
 from __future__ import annotations
 
@@ -152,6 +152,9 @@ def main():
                          "per-sequence, per-document and Algorithm 1 sharding; 'length' times forward and "
                          "backward of one GPU's sequence from 32K to 1M tokens")
     ap.add_argument("--cp", type=int, default=8, help="CP size of the sharding study")
+    ap.add_argument("--cp-backward", action="store_true",
+                    help="also time the CP rank's backward (per-block calls vs one call); off by default so that "
+                         "the backward kernels' launches in a trace of this command are the step's alone")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of it",
@@ -318,8 +321,11 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_merge:
-        (result["components"]["merge"], result["components"]["cp_rank_forward"],
-         result["components"]["cp_rank_backward"]) = bench_merge(api, torch, dev, upload, args.steps)
+        merge, cp_fwd, cp_bwd = bench_merge(api, torch, dev, upload, args.steps, args.cp_backward)
+        result["components"]["merge"] = merge
+        result["components"]["cp_rank_forward"] = cp_fwd
+        if cp_bwd is not None:
+            result["components"]["cp_rank_backward"] = cp_bwd
     if args.copy_calibration:
         # a streaming kernel of known size for scaling HBM byte counters: the
         # library's f32 -> bf16 conversion reads 1 GiB and writes 512 MiB
@@ -337,7 +343,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_merge(api, torch, dev, upload, steps):
+def bench_merge(api, torch, dev, upload, steps, cp_backward=False):
     """lse_merge of rank 3's per-block partials (CP = 8, chunks 3 and 12)."""
     from document_masked_attention_amd.workloads import make_config
     w = make_config(3)
@@ -480,6 +486,11 @@ def bench_merge(api, torch, dev, upload, steps):
         "merge_traffic": read_merge_traffic("merge_kernel_f32"),
         "note": "per-block forward calls writing float32 O, then lse_merge_f32 (bf16 output)"}})
     del jobs32
+    merge = {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
+             "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+             "bound": "hbm", "traffic": read_merge_traffic("merge_kernel")}
+    if not cp_backward:
+        return merge, cp_fwd, None
     # the rank's backward as a ring schedule runs it: per-(chunk, KV block)
     # calls with the merged O and LSE (dQ shares accumulated, Delta formed by
     # the first call of each chunk), beside one call over the whole KV range
@@ -525,9 +536,6 @@ def bench_merge(api, torch, dev, upload, steps):
     cp_bwd = {"workload": w.name, "useful_tflop": round(bwd_flop / 1e12, 3), **legs,
               "note": "scheduler + dQ + dK/dV kernel time; useful work 10*D*Hq*pairs"}
     del do_r, dq_r, dk_b, dv_b, dq1, dk1, dv1, ws_c
-    merge = {"workload": w.name, "partials_per_chunk": parts, "ms": round(ms, 4), "bytes": int(total_bytes),
-             "dense_bytes": int(dense_bytes), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-             "bound": "hbm", "traffic": read_merge_traffic("merge_kernel")}
     return merge, cp_fwd, cp_bwd
 
 
