@@ -108,16 +108,49 @@ def read_merge_traffic(key: str):
         return None
 
 
-def cpu_baseline(w, min_tokens: int = 14000):
-    """The oracle, as it stands, on whole documents covering the first
-    `min_tokens` tokens of the workload, one KV-head group (fwd + bwd)."""
-    import oracle
-    from document_masked_attention_amd.workloads import bf16_bits_to_f64
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def blas_threads() -> int | None:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        return None
+
+
+def merge_bytes(lse_parts: np.ndarray, d: int) -> float:
+    """The GPU merge's byte count for partials lse_parts [P, Hq, R]: every LSE
+    read, the O rows of partials with a finite LSE read, O and LSE written."""
+    p_c, hq, r = lse_parts.shape
+    finite = int(np.isfinite(lse_parts).sum())
+    return p_c * r * hq * 4 + finite * 2 * d + r * hq * (2 * d + 4)
+
+
+def cpu_baseline(w, min_tokens: int = 10000, merge_rows: int = 1024):
+    """The oracle, as it stands, on bounded samples of the same workloads, on
+    this host's cores (its numpy uses the BLAS threads it finds):
+      * fwd + bwd (the bench's value): whole documents covering the first
+        `min_tokens` tokens of the 131072-token bimodal mix, KV head 0 with its
+        query heads;
+      * fwd only: the same sample;
+      * lse_merge: the CP rank's (rank 3 of 8, chunks 3 and 12) partial shapes,
+        4 and 7 partials, on `merge_rows` rows of each chunk and all 32 heads,
+        with seeded normal partial O (bf16 values) and LSE (all finite, like
+        the GPU partials of that rank's canonical seed), bytes counted as the
+        GPU merge counts them."""
+    import oracle
+    from document_masked_attention_amd.workloads import bf16_bits_to_f64, f32_to_bf16_bits, make_config
+    cores = len(os.sched_getaffinity(0))
     cu = w.cu_seqlens
     end = int(cu[np.searchsorted(cu, min_tokens)])
     pos = np.arange(end)
@@ -127,15 +160,42 @@ def cpu_baseline(w, min_tokens: int = 14000):
     v = bf16_bits_to_f64(w.v(pos)[:, :1])
     do = bf16_bits_to_f64(w.do(pos)[:, :g])
     sub_cu = cu[cu <= end]
+    pairs = oracle.useful_pairs(sub_cu, [(0, end)], 0, end)
     t0 = time.perf_counter()
     oracle.attention_backward(q, k, v, do, sub_cu, [(0, end)], 0, end, w.scale)   # runs its own forward
     dt = time.perf_counter() - t0
-    pairs = oracle.useful_pairs(sub_cu, [(0, end)], 0, end)
-    flops = 14.0 * w.d * g * pairs
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fwd+bwd, first {end} tokens ({len(sub_cu) - 1} whole documents), KV head 0 with its "
-                      f"{g} query heads, float64 numpy, {dt:.1f} s",
-            "seconds": round(dt, 2), "cpu": platform.processor() or platform.machine()}
+    t0 = time.perf_counter()
+    oracle.attention_forward(q, k, v, sub_cu, [(0, end)], 0, end, w.scale)
+    dt_f = time.perf_counter() - t0
+    # merge: the rank's partial shapes (blocks its chunks need), sampled rows
+    w3 = make_config(3)
+    need = oracle.need_intervals(w3.cu_seqlens, w3.chunks, w3.kv_lo, w3.kv_hi)
+    rng = np.random.default_rng(3)
+    m_bytes, m_secs, parts = 0.0, 0.0, []
+    for (lo, hi) in need:
+        p_c = int((hi + w3.kv_block - 1) // w3.kv_block - lo // w3.kv_block)
+        parts.append(p_c)
+        o_p = bf16_bits_to_f64(f32_to_bf16_bits(rng.standard_normal((p_c, merge_rows, w3.hq, w3.d), np.float32)))
+        l_p = (3.0 * rng.standard_normal((p_c, w3.hq, merge_rows))).astype(np.float32).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.lse_merge(o_p, l_p)
+        m_secs += time.perf_counter() - t0
+        m_bytes += merge_bytes(l_p, w3.d)
+    bl = blas_threads()
+    return {"value": round(14.0 * w.d * g * pairs / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fwd+bwd, first {end} tokens ({len(sub_cu) - 1} whole documents) of the 131072-token "
+                      f"bimodal mix, KV head 0 with its {g} query heads, float64 numpy, {dt:.1f} s; flop counted "
+                      f"as the oracle executes it (14*D*Hq*pairs)",
+            "seconds": round(dt, 2), "cpu": cpu_model(), "blas_threads": bl,
+            "components": {
+                "fwd": {"value": round(4.0 * w.d * g * pairs / dt_f / 1e12, 6), "unit": "TFLOP/s",
+                        "seconds": round(dt_f, 2), "sample": "the same sample, forward only (4*D*Hq*pairs)"},
+                "merge": {"value": round(m_bytes / m_secs / 1e9, 3), "unit": "GB/s", "seconds": round(m_secs, 2),
+                          "bytes": int(m_bytes),
+                          "sample": f"oracle.lse_merge on the CP rank's partial shapes ({parts} partials), "
+                                    f"{merge_rows} rows per chunk, {w3.hq} heads, D={w3.d}; bytes as the GPU "
+                                    f"merge counts them"}}}
 
 
 def main():

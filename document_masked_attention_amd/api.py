@@ -13,7 +13,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdocmask.so")
+# DOCMASK_LIBRARY names another build of the same library (e.g. the
+# host-sanitized one); by default the in-tree libdocmask.so
+_LIB_PATH = os.environ.get("DOCMASK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                               "libdocmask.so")
 _lib = None
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE_INPUT = 0, -1, -2, -3, -4, -5

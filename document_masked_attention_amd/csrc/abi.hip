@@ -96,7 +96,11 @@ Layout bwd_layout(const docmask_chunk* chunks, int32_t n_chunks, const Problem& 
   L.n_kt = (pr.tkv + (int64_t)kBwdBK - 1) / kBwdBK;
   L.n_qt2 = count_qtiles(chunks, n_chunks, dq_rows_per_tile(pr.group));
   L.n_kt2 = (pr.tkv + (int64_t)kDqBK - 1) / kDqBK;
+  // Delta first, right after the header: its offset depends on nothing but
+  // the header, so a later call with DOCMASK_DELTA_READY over a KV block of a
+  // different length finds it where the earlier call stored it
   size_t off = kAlign;
+  L.delta = off;  off = align_up(off + (size_t)hq * pr.tq * 4);
   L.plan_q = off; off = align_up(off + (size_t)L.n_qt * QP_WORDS * 4);
   L.kvdesc = off; off = align_up(off + (size_t)L.n_kt * 4 * 4);
   L.key_kv = off; off = align_up(off + (size_t)L.n_kt * 4);
@@ -108,7 +112,6 @@ Layout bwd_layout(const docmask_chunk* chunks, int32_t n_chunks, const Problem& 
   L.lpt_q = off;  off = align_up(off + (size_t)L.n_qt2 * 4);
   const int64_t hist_n = (L.n_qt > L.n_kt2 ? L.n_qt : L.n_kt2) + 2;
   L.hist = off;   off = align_up(off + (size_t)hist_n * 4);
-  L.delta = off;  off = align_up(off + (size_t)hq * pr.tq * 4);
   L.total = off;
   return L;
 }
@@ -193,7 +196,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, const int3
   Problem pr;
   int st = check_shape(n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, &pr);
   if (st != DOCMASK_OK) return st;
-  if (!cu_seqlens_dev || !std::isfinite(softmax_scale)) return DOCMASK_EINVAL;
+  if (!cu_seqlens_dev || !std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DOCMASK_EINVAL;
   if (pr.tq == 0) return DOCMASK_OK;
   void* out = o32 ? static_cast<void*>(o32) : o;
   if (!q || !out || !lse || !aligned16(q) || !aligned16(out) || !aligned4(lse)) return DOCMASK_EINVAL;
@@ -259,7 +262,7 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   Problem pr;
   int st = check_shape(n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, &pr);
   if (st != DOCMASK_OK) return st;
-  if (!cu_seqlens_dev || !std::isfinite(softmax_scale)) return DOCMASK_EINVAL;
+  if (!cu_seqlens_dev || !std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DOCMASK_EINVAL;
   if (flags & ~(DOCMASK_ACCUMULATE_DQ | DOCMASK_DELTA_READY)) return DOCMASK_EINVAL;
   if (pr.tq > 0 && (!q || !o || !lse || !d_o || !dq || !aligned16(q) || !aligned16(o) || !aligned16(d_o) ||
                     !aligned16(dq) || !aligned4(lse)))

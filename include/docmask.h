@@ -29,8 +29,11 @@
  *    LSE = -inf.
  *  - Every pointer argument named *_dev or a tensor is device memory owned by
  *    the caller; chunk arrays are host memory read during the call.  The
- *    library allocates nothing and keeps no state between calls; it is
- *    re-entrant.  Calls on one stream run in order; calls that share a
+ *    attention, merge, scheduler and exchange calls allocate nothing and
+ *    keep no state between calls (everything a call needs lives in its
+ *    arguments and the caller's workspace); they are re-entrant.  The only
+ *    process-wide state is the opt-in kernel timer below (its event pool and
+ *    totals).  Calls on one stream run in order; calls that share a
  *    workspace must not overlap.
  *  - Work is enqueued on `stream` (0 = the null stream).  The return value
  *    reports argument validation (checked on the host before anything is
@@ -39,7 +42,9 @@
  *    docmask_check_errors.
  *  - Tensor pointers must be 16-byte aligned; D must be 64 or 128;
  *    Hq % Hkv == 0; chunks must be disjoint, in ascending position order,
- *    and at most DOCMASK_MAX_CHUNKS.
+ *    and at most DOCMASK_MAX_CHUNKS; softmax_scale must be finite and
+ *    positive (scale 0 would turn masked scores into NaN, a negative one
+ *    would reverse the softmax reference), else DOCMASK_EINVAL.
  */
 #ifndef DOCMASK_H
 #define DOCMASK_H
@@ -80,7 +85,10 @@ enum {
   DOCMASK_ACCUMULATE_DQ = 1,
   /* The workspace already holds Delta = rowsum(dO * O) from an earlier call
    * with the same o, d_o, chunks and heads (e.g. the previous KV block of a
-   * split-KV backward): skip recomputing it. */
+   * split-KV backward): skip recomputing it.  Delta sits at a fixed place in
+   * the workspace that depends only on Hq and the chunk rows, so the earlier
+   * call may have held a KV range of any length (the workspace must still be
+   * large enough for every call that uses it). */
   DOCMASK_DELTA_READY = 2
 };
 

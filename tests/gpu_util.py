@@ -1,4 +1,9 @@
-"""Helpers shared by the GPU parity tests (device transfer and comparisons)."""
+"""Helpers shared by the GPU parity tests (device transfer, comparisons and
+the record of measured errors)."""
+import json
+import os
+import time
+
 import numpy as np
 import torch
 
@@ -36,3 +41,36 @@ def assert_close(got, want, tol, what):
     err = np.abs(got[fin] - want[fin]).max() if fin.any() else 0.0
     assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
     return err
+
+
+def host_cores() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def gpu_ms(fn):
+    """(result, milliseconds) of fn() between two events on the current stream."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    out = fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return out, e0.elapsed_time(e1)
+
+
+def timed_s(fn):
+    """(result, wall seconds) of fn() on the host."""
+    t0 = time.perf_counter()
+    out = fn()
+    return out, time.perf_counter() - t0
+
+
+def record(**row):
+    """Append one row of measured parity errors (and timings) as a JSON line to
+    the file named by DOCMASK_PARITY_LOG; nothing happens when it is unset."""
+    path = os.environ.get("DOCMASK_PARITY_LOG")
+    if not path:
+        return
+    row = {k: (float(v) if isinstance(v, (np.floating, np.integer)) else v) for k, v in row.items()}
+    with open(path, "a") as f:
+        f.write(json.dumps(row) + "\n")

@@ -64,6 +64,13 @@ def test_fwd_argument_validation(lib):
     assert _fwd(lib, o=None) == api.EINVAL
     assert _fwd(lib, k=None) == api.EINVAL
     assert _fwd(lib, scale=float("nan")) == api.EINVAL
+    assert _fwd(lib, scale=float("inf")) == api.EINVAL
+    assert _fwd(lib, scale=0.0) == api.EINVAL                          # masked scores would become NaN
+    assert _fwd(lib, scale=-0.1) == api.EINVAL                         # would reverse the softmax reference
+    arr, n = api._chunks([(0, 100)])
+    for bad_scale in (0.0, -0.1, float("nan")):
+        assert lib.docmask_attn_fwd_f32out(FAKE, FAKE, FAKE, FAKE, 3, arr, n, 0, 100, 4, 2, 128, bad_scale, FAKE,
+                                           FAKE, FAKE, 1 << 30, None) == api.EINVAL
     assert _fwd(lib, ws=None) == api.EWORKSPACE
     assert _fwd(lib, ws_bytes=16) == api.EWORKSPACE
     assert _fwd(lib, chunks=()) == api.OK                              # no query rows: nothing to do
@@ -77,6 +84,10 @@ def test_bwd_and_merge_validation(lib):
     bad = list(args)
     bad[16] = MIS                                                                 # misaligned dq
     assert lib.docmask_attn_bwd(*bad, 0, FAKE, 1 << 30, None) == api.EINVAL
+    for bad_scale in (0.0, -0.1, float("nan"), float("-inf")):
+        bad = list(args)
+        bad[15] = bad_scale
+        assert lib.docmask_attn_bwd(*bad, 0, FAKE, 1 << 30, None) == api.EINVAL
     assert lib.lse_merge(FAKE, FAKE, 0, 10, 4, 128, FAKE, FAKE, None) == api.EINVAL
     assert lib.lse_merge(FAKE, FAKE, 2, 10, 4, 32, FAKE, FAKE, None) == api.EUNSUPPORTED
     assert lib.lse_merge(MIS, FAKE, 2, 10, 4, 128, FAKE, FAKE, None) == api.EINVAL
@@ -92,6 +103,9 @@ def test_workspace_sizes(lib):
     assert api.workspace_size(api.OP_FWD, 3, [(0, 4096)], 0, 4096, 32, 8, 96) == 0
     assert api.workspace_size(7, 3, [(0, 4096)], 0, 4096, 32, 8, 128) == 0
     assert api.schedule_workspace_size([(0, 100)], 0, 100, 16, 16) > 0
+    # the backward workspace grows with the KV range, Delta [Hq, Tq] does not
+    small = api.workspace_size(api.OP_BWD, 3, [(0, 4096)], 0, 100, 32, 8, 128)
+    assert 32 * 4096 * 4 < small < bwd
     assert api.schedule_workspace_size([(0, 100)], 0, 100, 0, 16) == 0
 
 

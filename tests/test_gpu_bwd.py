@@ -7,6 +7,8 @@ afford: its last rows as the query chunk against the document's whole key
 range.  dQ of those rows and dK/dV of the keys inside that tail depend only on
 the tail rows (a key is attended only by rows at or after it in its document),
 so the sub-problem's values are exact there."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -14,17 +16,40 @@ import torch
 import oracle
 from document_masked_attention_amd import api
 from document_masked_attention_amd.workloads import custom_workload, make_config, random_lengths, Workload
-from gpu_util import to_dev, bf16_to_np, f64, assert_close, O_TOL
+from gpu_util import to_dev, bf16_to_np, f64, assert_close, O_TOL, gpu_ms, timed_s, record, host_cores
 
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_fwd_bwd(w: Workload, q, k, v, do, accumulate=False):
+def _gpu_fwd_bwd(w: Workload, q, k, v, do, accumulate=False, with_ms=False):
     qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
     o, lse = api.attn_fwd(qd, kd, vd, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
-    dq, dk, dv = api.attn_bwd(qd, kd, vd, o, lse, dod, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
-    torch.cuda.synchronize()
-    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    (dq, dk, dv), ms = gpu_ms(lambda: api.attn_bwd(qd, kd, vd, o, lse, dod, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi,
+                                                   w.scale))
+    out = (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+    return (*out, ms) if with_ms else out
+
+
+def _oracle_backward_by_head(q, k, v, do, cu, chunks, kv_lo, kv_hi, scale, tag):
+    """oracle.attention_backward for one KV head and its G query heads, one
+    oracle call per query head in parallel threads (BLAS threads shared out);
+    dQ per head, dK and dV summed over the heads (each head's share of the
+    group's gradient is exactly that head's call)."""
+    from threadpoolctl import threadpool_limits
+    g = q.shape[1]
+    workers = max(1, min(g, host_cores()))
+
+    def one(h):
+        r, secs = timed_s(lambda: oracle.attention_backward(q[:, h:h + 1], k, v, do[:, h:h + 1], cu, chunks, kv_lo,
+                                                             kv_hi, scale))
+        print(f"[bwd] {tag}: oracle query head {h} done ({secs:.1f} s)", flush=True)
+        return r
+
+    with threadpool_limits(limits=max(1, host_cores() // workers)):
+        with ThreadPoolExecutor(workers) as ex:
+            res = list(ex.map(one, range(g)))
+    return (np.concatenate([r[0] for r in res], axis=1), np.sum([r[1] for r in res], axis=0),
+            np.sum([r[2] for r in res], axis=0))
 
 
 def _check_small(w: Workload, tag):
@@ -91,6 +116,45 @@ def test_split_kv_backward_sums_to_full():
     assert_close(dv.cpu().numpy(), wv, O_TOL, "split dV")
 
 
+def test_split_kv_backward_ragged_last_block_delta_ready():
+    """Split-KV backward whose second KV block is shorter than the first:
+    Delta formed by the first call ([0, 8192)) and reused by the second
+    ([8192, 12000), DOCMASK_DELTA_READY) through one workspace, dQ shares
+    added; equal to one call over [0, 12000) and to the oracle on sampled rows
+    and keys."""
+    total = 12000
+    w = custom_workload(31, random_lengths(np.random.default_rng(31), total, 5000), 8, 2, 128, backward=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    cu = w.cu_seqlens
+    print(f"[bwd] ragged split-KV with Delta reuse: {len(w.lengths)} documents, blocks [0,8192) [8192,{total})",
+          flush=True)
+    o, lse = api.attn_fwd(qd, kd, vd, cu, w.chunks, 0, total, w.scale)
+    dq1, dk1, dv1 = api.attn_bwd(qd, kd, vd, o, lse, dod, cu, w.chunks, 0, total, w.scale)
+    ws = torch.empty(api.workspace_size(api.OP_BWD, len(w.lengths), w.chunks, 0, 8192, w.hq, w.hkv, w.d),
+                     dtype=torch.uint8, device="cuda")
+    dq = torch.empty_like(dq1)
+    dk = torch.empty_like(dk1)
+    dv = torch.empty_like(dv1)
+    for i, (x, y) in enumerate([(0, 8192), (8192, total)]):
+        api.attn_bwd(qd, kd[x:y], vd[x:y], o, lse, dod, cu, w.chunks, x, y, w.scale, dq=dq, dk=dk[x:y],
+                     dv=dv[x:y], accumulate_dq=i > 0, delta_ready=i > 0, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(dq.cpu().numpy(), dq1.cpu().numpy(), 1e-4, "split vs single dQ")
+    assert_close(dk.cpu().numpy(), dk1.cpu().numpy(), 1e-5, "split vs single dK")
+    assert_close(dv.cpu().numpy(), dv1.cpu().numpy(), 1e-5, "split vs single dV")
+    rows = np.unique(np.concatenate([np.arange(0, total, 997), [total - 1]]))
+    wq, _, _ = oracle.attention_backward(f64(q[rows]), f64(k), f64(v), f64(do[rows]), cu,
+                                         [(int(r), 1) for r in rows], 0, total, w.scale)
+    assert_close(dq.cpu().numpy()[rows], wq, O_TOL, "split dQ vs oracle")
+    # dK / dV of the second block's keys: every row of their documents at or after them
+    a = int(cu[np.searchsorted(cu, 8192, side="right") - 1])
+    wq, wk, wv = oracle.attention_backward(f64(q[a:]), f64(k[a:]), f64(v[a:]), f64(do[a:]), cu, [(a, total - a)],
+                                           a, total, w.scale)
+    assert_close(dk.cpu().numpy()[8192:], wk[8192 - a:], O_TOL, "split dK vs oracle (second block)")
+    assert_close(dv.cpu().numpy()[8192:], wv[8192 - a:], O_TOL, "split dV vs oracle (second block)")
+
+
 @pytest.mark.parametrize("cfg,seed", [(4, None), (5, None), (4, 11), (4, 12), (4, 13), (5, 12)])
 def test_full_size_sampled_documents(cfg, seed):
     """Canonical seeds (the config index) and the extra seeds 11-13."""
@@ -104,6 +168,7 @@ def test_full_size_sampled_documents(cfg, seed):
     docs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1]), int(order[-2])})
     rng = np.random.default_rng(cfg)
     g = w.hq // w.hkv
+    errs = []
     for doc in docs:
         a, b = int(cu[doc]), int(cu[doc + 1])
         tail = min(b - a, 256)
@@ -116,9 +181,51 @@ def test_full_size_sampled_documents(cfg, seed):
         sk = f64(k[a:b, kvh:kvh + 1])
         sv = f64(v[a:b, kvh:kvh + 1])
         wq, wk, wv = oracle.attention_backward(sq, sk, sv, sdo, cu, [(t0, tail)], a, b, w.scale)
-        assert_close(dq[t0:b][:, heads], wq, O_TOL, f"doc {doc} dQ")
-        assert_close(dk[t0:b, kvh:kvh + 1], wk[t0 - a:], O_TOL, f"doc {doc} dK")
-        assert_close(dv[t0:b, kvh:kvh + 1], wv[t0 - a:], O_TOL, f"doc {doc} dV")
+        errs.append((assert_close(dq[t0:b][:, heads], wq, O_TOL, f"doc {doc} dQ"),
+                     assert_close(dk[t0:b, kvh:kvh + 1], wk[t0 - a:], O_TOL, f"doc {doc} dK"),
+                     assert_close(dv[t0:b, kvh:kvh + 1], wv[t0 - a:], O_TOL, f"doc {doc} dV")))
+    e = np.max(errs, axis=0)
+    record(config=cfg, seed=w.seed, check="backward, document tails",
+           compared=f"last <= 256 rows and keys of {len(docs)} documents, one KV-head group each",
+           err_dQ=e[0], err_dK=e[1], err_dV=e[2], cores=host_cores())
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("cfg,ranks", [(4, (1,)), (5, (1, 2))])
+def test_full_size_whole_long_documents(cfg, ranks):
+    """Whole long documents of the full-size workloads (canonical seeds): the
+    longest (and, for the 131072-token mix, the second-longest) document,
+    every row and every key, one KV-head group.  A key is attended only by
+    rows of its own document, so the oracle sub-problem chunk = [a, b),
+    KV = [a, b) gives that document's exact dQ, dK and dV; this covers the
+    key-major work items' whole walks over the document's query blocks
+    (production guide, "Step 1: Establish a Single-GPU Numerical Baseline":
+    long sequences, not only short ones)."""
+    w = make_config(cfg)
+    print(f"[bwd] config {cfg} seed {w.seed}: generating inputs", flush=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    dq, dk, dv, ms = _gpu_fwd_bwd(w, q, k, v, do, with_ms=True)
+    cu = w.cu_seqlens
+    lengths = np.diff(cu)
+    order = np.argsort(-lengths, kind="stable")
+    g = w.hq // w.hkv
+    for rank in ranks:
+        doc = int(order[rank - 1])
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        kvh = (3 * rank + cfg) % w.hkv
+        heads = np.arange(kvh * g, (kvh + 1) * g)
+        tag = f"config {cfg} doc {doc} [{a},{b}) ({b - a} tokens) kv head {kvh}"
+        print(f"[bwd] {tag}: oracle over the whole document", flush=True)
+        (wq, wk, wv), secs = timed_s(lambda: _oracle_backward_by_head(
+            f64(q[a:b][:, heads]), f64(k[a:b, kvh:kvh + 1]), f64(v[a:b, kvh:kvh + 1]), f64(do[a:b][:, heads]), cu,
+            [(a, b - a)], a, b, w.scale, tag))
+        eq = assert_close(dq[a:b][:, heads], wq, O_TOL, f"{tag} dQ")
+        ek = assert_close(dk[a:b, kvh:kvh + 1], wk, O_TOL, f"{tag} dK")
+        ev = assert_close(dv[a:b, kvh:kvh + 1], wv, O_TOL, f"{tag} dV")
+        print(f"[bwd] {tag}: max abs error dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e} (oracle {secs:.1f} s)", flush=True)
+        record(config=cfg, seed=w.seed, check=f"backward, whole document of {b - a} tokens (rank {rank} by length)",
+               compared=f"all {b - a} rows and keys, KV head {kvh} with its {g} query heads",
+               err_dQ=eq, err_dK=ek, err_dV=ev, gpu_ms=round(ms, 3), oracle_s=round(secs, 2), cores=host_cores())
 
 
 def test_one_million_tokens_document_tails():

@@ -14,24 +14,30 @@ import oracle
 from document_masked_attention_amd import api
 from document_masked_attention_amd.workloads import (custom_workload, make_config, random_lengths,
                                                      cu_from_lengths, Workload)
-from gpu_util import to_dev, bf16_to_np, f64, assert_close, O_TOL, LSE_TOL
+from gpu_util import (to_dev, bf16_to_np, f64, assert_close, O_TOL, LSE_TOL, gpu_ms, timed_s, record,
+                      host_cores)
 
 pytestmark = pytest.mark.gpu
 
 
-def _run_and_compare(w: Workload, rows=None, tag=""):
+def _run_and_compare(w: Workload, rows=None, tag="", config=None):
+    """GPU forward of the whole workload against the oracle on `rows` (all by
+    default); with `config`, the measured errors and times are recorded."""
     print(f"[fwd] {tag} {w.name} seed={w.seed} T={w.total} tq={w.tq} h={w.hq}/{w.hkv} d={w.d} "
           f"chunks={w.chunks[:4]} kv=[{w.kv_lo},{w.kv_hi})", flush=True)
     q, k, v = w.q(), w.k(), w.v()
-    o, lse = api.attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
-    torch.cuda.synchronize()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    (o, lse), ms = gpu_ms(lambda: api.attn_fwd(qd, kd, vd, w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale))
     o_np = bf16_to_np(o)
     lse_np = lse.cpu().numpy().astype(np.float64)
     sel = np.arange(w.tq) if rows is None else np.asarray(rows)
-    want_o, want_l = oracle.attention_forward(f64(q), f64(k), f64(v), w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi,
-                                              w.scale, rows=sel)
-    assert_close(o_np[sel], want_o, O_TOL, f"{tag} O")
-    assert_close(lse_np[:, sel], want_l, LSE_TOL, f"{tag} LSE")
+    (want_o, want_l), secs = timed_s(lambda: oracle.attention_forward(f64(q), f64(k), f64(v), w.cu_seqlens, w.chunks,
+                                                                       w.kv_lo, w.kv_hi, w.scale, rows=sel))
+    eo = assert_close(o_np[sel], want_o, O_TOL, f"{tag} O")
+    el = assert_close(lse_np[:, sel], want_l, LSE_TOL, f"{tag} LSE")
+    if config is not None:
+        record(config=config, seed=w.seed, check="forward", compared=f"{sel.size} of {w.tq} rows, all heads",
+               err_O=eo, err_LSE=el, gpu_ms=round(ms, 3), oracle_s=round(secs, 2), cores=host_cores())
     return q, k, v, o_np, lse_np
 
 
@@ -94,7 +100,7 @@ def test_empty_kv_range_rows():
 
 
 def test_config1_full():
-    _run_and_compare(make_config(1), tag="config 1")
+    _run_and_compare(make_config(1), tag="config 1", config=1)
 
 
 def _sample_rows(w: Workload, n: int, seed: int):
@@ -113,7 +119,8 @@ def _sample_rows(w: Workload, n: int, seed: int):
 def test_full_size_sampled_rows(cfg, seed):
     """Canonical seeds (the config index) and the extra seeds 11-13."""
     w = make_config(cfg, seed)
-    _run_and_compare(w, rows=_sample_rows(w, 128 if cfg < 5 else 64, cfg), tag=f"config {cfg} seed {w.seed} sampled")
+    _run_and_compare(w, rows=_sample_rows(w, 128 if cfg < 5 else 64, cfg), tag=f"config {cfg} seed {w.seed} sampled",
+                     config=cfg)
 
 
 @pytest.mark.parametrize("seed", [None, 11])
@@ -146,10 +153,13 @@ def test_cp_rank_partials_and_merge(seed):
         assert_close(l_np, l_full.cpu().numpy(), LSE_TOL, "merged vs full-range LSE")
         rows = np.unique(np.concatenate([np.arange(0, n, 97), [n - 1]]))
         wq = f64(q[row0 + rows])
-        want_o, want_l = oracle.attention_forward(wq, f64(k), f64(v), cu, [(g + int(r), 1) for r in rows],
-                                                  w.kv_lo, w.kv_hi, w.scale)
-        assert_close(o_np[rows], want_o, O_TOL, f"chunk {g} merged O")
-        assert_close(l_np[:, rows], want_l, LSE_TOL, f"chunk {g} merged LSE")
+        (want_o, want_l), secs = timed_s(lambda: oracle.attention_forward(
+            wq, f64(k), f64(v), cu, [(g + int(r), 1) for r in rows], w.kv_lo, w.kv_hi, w.scale))
+        eo = assert_close(o_np[rows], want_o, O_TOL, f"chunk {g} merged O")
+        el = assert_close(l_np[:, rows], want_l, LSE_TOL, f"chunk {g} merged LSE")
+        record(config=3, seed=w.seed, check=f"per-block forward + lse_merge, chunk at {g} ({len(blocks)} partials)",
+               compared=f"{rows.size} of {n} rows, all heads", err_O=eo, err_LSE=el, oracle_s=round(secs, 2),
+               cores=host_cores())
         row0 += n
 
 
