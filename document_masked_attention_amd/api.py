@@ -19,7 +19,8 @@ _LIB_PATH = os.environ.get("DOCMASK_LIBRARY") or os.path.join(os.path.dirname(os
                                                                "libdocmask.so")
 _lib = None
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE_INPUT = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE_INPUT, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 4 << 20
 OP_FWD, OP_BWD = 1, 2
 ACCUMULATE_DQ = 1
 DELTA_READY = 2
@@ -54,6 +55,8 @@ _SIGNATURES = {
                                         _i32, _f32, _vp, _vp, _vp, ctypes.c_int, _vp, _sz, _vp]),
     "lse_merge": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "lse_merge_f32": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "docmask_attn_fwd_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                _f32, _vp, _vp, _vp]),
     "docmask_attn_fwd_f32out": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                _f32, _vp, _vp, _vp, _sz, _vp]),
     "docmask_check_errors": (ctypes.c_int, [_vp, _vp]),
@@ -204,6 +207,26 @@ def attn_fwd(q, k, v, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float |
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_docs, arr, n, kv_lo, kv_hi, hq, hkv, d,
             float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "docmask_attn_fwd_f32out" if f32_out else "docmask_attn_fwd")
+    return out, lse
+
+
+def attn_fwd_noalloc(q, k, v, cu_seqlens, chunks, kv_lo: int, kv_hi: int, scale: float | None = None, out=None,
+                     lse=None):
+    """docmask_attn_fwd_noalloc: the forward without a workspace (the library's
+    static scratch); out and lse must be given when the caller cannot allocate."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    cu = _dev_i32(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    arr, n = _chunks(chunks)
+    st = lib().docmask_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), cu.numel() - 1, arr, n, kv_lo, kv_hi,
+                                        hq, hkv, d, float(scale), _ptr(out), _ptr(lse), _stream())
+    _check(st, "docmask_attn_fwd_noalloc")
     return out, lse
 
 

@@ -6,8 +6,17 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 using namespace docmask;
+
+// Scratch of docmask_attn_fwd_noalloc: the forward's workspace (error word,
+// tile plans, LPT keys and order, histogram) as one static device array, so
+// that entry point never allocates.  Each GPU the library runs on holds its
+// own copy until the process ends.  Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol): it uses the
+// device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[DOCMASK_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -244,6 +253,45 @@ int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
                        o, nullptr, lse, workspace, workspace_bytes, stream);
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with it current) and kept per device.
+static int noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DOCMASK_EHIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DOCMASK_EHIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return DOCMASK_OK;
+}
+
+int docmask_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                             int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
+                             int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o,
+                             float* lse, hipStream_t stream) {
+  Problem pr;
+  int st = check_shape(n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, &pr);
+  if (st != DOCMASK_OK) return st;
+  if (!cu_seqlens_dev || !std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return DOCMASK_EINVAL;
+  if (pr.tq == 0) return DOCMASK_OK;
+  const size_t need = fwd_layout(chunks, n_chunks, pr).total;
+  if (need > DOCMASK_NOALLOC_SCRATCH_BYTES) return DOCMASK_ESCRATCH;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != DOCMASK_OK) return st;
+  // every region of the workspace the kernels read is written earlier in the
+  // same call (the error word by the validation kernel), so the previous
+  // call's contents need no clearing
+  return attn_fwd_impl(q, k, v, cu_seqlens_dev, n_docs, chunks, n_chunks, kv_lo, kv_hi, hq, hkv, d, softmax_scale, o,
+                       nullptr, lse, ws, DOCMASK_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int docmask_attn_fwd_f32out(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
                             int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
                             int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, float* o,
@@ -387,6 +435,8 @@ const char* docmask_strerror(int status) {
     case DOCMASK_EWORKSPACE: return "workspace missing or too small";
     case DOCMASK_EHIP: return "HIP launch failed";
     case DOCMASK_EDEVICE_INPUT: return "malformed cu_seqlens (not starting at 0, decreasing, or too short)";
+    case DOCMASK_ESCRATCH:
+      return "problem too large for the allocation-free forward's static scratch (DOCMASK_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

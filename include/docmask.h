@@ -71,7 +71,8 @@ typedef enum {
   DOCMASK_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. D not in {64, 128}) */
   DOCMASK_EWORKSPACE = -3,    /* workspace missing or smaller than docmask_workspace_size */
   DOCMASK_EHIP = -4,          /* a HIP launch failed */
-  DOCMASK_EDEVICE_INPUT = -5  /* reported by docmask_check_errors: malformed cu_seqlens */
+  DOCMASK_EDEVICE_INPUT = -5, /* reported by docmask_check_errors: malformed cu_seqlens */
+  DOCMASK_ESCRATCH = -6       /* docmask_attn_fwd_noalloc: problem exceeds its static scratch */
 } docmask_status;
 
 /* Operations a workspace is sized for. */
@@ -136,6 +137,27 @@ int docmask_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
                      int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
                      int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o,
                      float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, kernels and
+ * arguments as docmask_attn_fwd, with the workspace replaced by a static
+ * device array of DOCMASK_NOALLOC_SCRATCH_BYTES inside the library (one per
+ * GPU, held until the process ends; enough for about three million query
+ * rows).  A problem whose docmask_workspace_size(DOCMASK_OP_FWD, ...)
+ * exceeds it returns DOCMASK_ESCRATCH before anything is enqueued.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * the caller still owns q, k, v, cu_seqlens, o and lse.  Every call on one
+ * GPU shares that GPU's array: calls that may overlap on one GPU (two
+ * streams, two threads) race and must be serialised by the caller.  Device
+ * input errors are recorded in the array's first word; this entry point has
+ * no error read-back of its own (use docmask_attn_fwd with a workspace and
+ * docmask_check_errors to diagnose malformed cu_seqlens). */
+#define DOCMASK_NOALLOC_SCRATCH_BYTES (4u << 20)
+int docmask_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                             int32_t n_docs, const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo,
+                             int32_t kv_hi, int32_t hq, int32_t hkv, int32_t d, float softmax_scale, void* o,
+                             float* lse, hipStream_t stream);
 
 /* Forward with O written as float32 [Tq][Hq][D] (otherwise identical to
  * docmask_attn_fwd, same workspace): partial results for lse_merge_f32, so

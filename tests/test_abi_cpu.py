@@ -76,6 +76,25 @@ def test_fwd_argument_validation(lib):
     assert _fwd(lib, chunks=()) == api.OK                              # no query rows: nothing to do
 
 
+def test_noalloc_forward_validation(lib):
+    """Checked on the host before the static scratch is looked up."""
+    def call(chunks=((0, 100),), scale=0.1, d=128, cu=FAKE, hq=4, hkv=2):
+        arr, n = api._chunks(list(chunks))
+        return lib.docmask_attn_fwd_noalloc(FAKE, FAKE, FAKE, cu, 3, arr, n, 0, 100, hq, hkv, d, scale, FAKE, FAKE,
+                                            None)
+    assert call(scale=0.0) == api.EINVAL
+    assert call(scale=float("nan")) == api.EINVAL
+    assert call(cu=None) == api.EINVAL
+    assert call(d=96) == api.EUNSUPPORTED
+    assert call(hq=6, hkv=4) == api.EINVAL
+    assert call(chunks=()) == api.OK                                   # no query rows: nothing to do
+    # the forward workspace of 2^22 query rows (>= 40 bytes per 32-row tile) exceeds the static scratch
+    big = [(0, 1 << 22)]
+    assert api.workspace_size(api.OP_FWD, 3, big, 0, 100, 16, 2, 128) > api.NOALLOC_SCRATCH_BYTES
+    assert call(chunks=big, hq=16) == api.ESCRATCH
+    assert "static scratch" in api.strerror(api.ESCRATCH)
+
+
 def test_bwd_and_merge_validation(lib):
     arr, n = api._chunks([(0, 100)])
     args = [FAKE] * 7 + [3, arr, n, 0, 100, 4, 2, 128, 0.1, FAKE, FAKE, FAKE]
@@ -110,7 +129,7 @@ def test_workspace_sizes(lib):
 
 
 def test_strerror(lib):
-    for s in (api.OK, api.EINVAL, api.EUNSUPPORTED, api.EWORKSPACE, api.EHIP, api.EDEVICE_INPUT):
+    for s in (api.OK, api.EINVAL, api.EUNSUPPORTED, api.EWORKSPACE, api.EHIP, api.EDEVICE_INPUT, api.ESCRATCH):
         assert api.strerror(s)
     assert "unknown" in api.strerror(123)
 
