@@ -136,7 +136,7 @@ def merge_bytes(lse_parts: np.ndarray, d: int) -> float:
     return p_c * r * hq * 4 + finite * 2 * d + r * hq * (2 * d + 4)
 
 
-def cpu_baseline(w, min_tokens: int = 10000, merge_rows: int = 1024):
+def cpu_baseline(w, min_tokens: int = 10000, merge_rows: int = 8192):
     """The oracle, as it stands, on bounded samples of the same workloads, on
     this host's cores (its numpy uses the BLAS threads it finds):
       * fwd + bwd (the bench's value): whole documents covering the first
@@ -144,7 +144,8 @@ def cpu_baseline(w, min_tokens: int = 10000, merge_rows: int = 1024):
         query heads;
       * fwd only: the same sample;
       * lse_merge: the CP rank's (rank 3 of 8, chunks 3 and 12) partial shapes,
-        4 and 7 partials, on `merge_rows` rows of each chunk and all 32 heads,
+        4 and 7 partials, on `merge_rows` rows of each chunk (default: all
+        8192, the GPU merge's whole workload) and all 32 heads,
         with seeded normal partial O (bf16 values) and LSE (all finite, like
         the GPU partials of that rank's canonical seed), bytes counted as the
         GPU merge counts them."""
