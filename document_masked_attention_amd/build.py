@@ -59,10 +59,41 @@ def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
     return out
 
 
+BWD_ASM = os.path.join(BUILD, "bwd-gfx950.s")
+
+
+def check_inline_mfma_wait_states(verbose: bool = False) -> int:
+    """Generate the gfx950 assembly of bwd.hip and check the dK/dV kernel's
+    inline-assembly MFMAs (see isa_check); raises on any violation.  Returns
+    the number of MFMAs checked."""
+    from . import isa_check
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "--cuda-device-only", "-S",
+           os.path.join(CSRC, "bwd.hip"), "-o", BWD_ASM]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for bwd.hip:\n{r.stderr}")
+    asm = open(BWD_ASM).read()
+    syms = isa_check.kernel_symbols(asm)
+    if not syms:
+        raise RuntimeError("no dK/dV kernel found in the generated assembly")
+    total, bad = 0, []
+    for sym in syms:
+        n, v = isa_check.check(asm, sym)
+        total += n
+        bad += v
+    if bad:
+        raise RuntimeError("inline MFMA results touched inside the wait-state window:\n" + "\n".join(bad))
+    if verbose:
+        print(f"wait states of {total} inline MFMAs checked in {len(syms)} dK/dV kernels")
+    return total
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        chk = ex.submit(check_inline_mfma_wait_states, verbose)
         objs = list(ex.map(_compile, SOURCES))
+        chk.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
