@@ -208,10 +208,11 @@ def main():
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the f32->bf16 conversion over 1 GiB (reference for HBM byte counters)")
-    ap.add_argument("--study", choices=["sharding", "length"],
+    ap.add_argument("--study", choices=["sharding", "length", "power"],
                     help="instead of the step benchmark: 'sharding' times every CP rank's forward under "
                          "per-sequence, per-document and Algorithm 1 sharding; 'length' times forward and "
-                         "backward of one GPU's sequence from 32K to 1M tokens")
+                         "backward of one GPU's sequence from 32K to 1M tokens; 'power' samples board power and "
+                         "clocks (amd-smi) while the forward, the backward and a bf16 GEMM run back to back")
     ap.add_argument("--cp", type=int, default=8, help="CP size of the sharding study")
     ap.add_argument("--cp-backward", action="store_true",
                     help="also time the CP rank's backward (per-block calls vs one call); off by default so that "
@@ -226,6 +227,9 @@ def main():
         return
     if args.study == "length":
         study_length(max(args.steps, 3))
+        return
+    if args.study == "power":
+        study_power()
         return
 
     import torch
@@ -401,6 +405,90 @@ def main():
         log("[bench] cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)
         log(f"[bench] cpu baseline {result['cpu_baseline']['seconds']} s")
+    print(json.dumps(result), flush=True)
+
+
+def study_power(seconds: float = 4.0):
+    """Board power and GFX clocks (amd-smi, sampled about every 0.3 s) while
+    the step's forward, its backward and, as a reference of what the chip
+    sustains on pure matrix work, a bf16 8192^3 GEMM (torch.matmul) each run
+    back to back for `seconds`; one JSON line with the medians per phase."""
+    import statistics
+    import subprocess
+    import threading
+    import torch
+    from document_masked_attention_amd import api
+    from document_masked_attention_amd.workloads import make_config
+    api.lib()
+    dev = torch.device("cuda:0")
+    samples, stop, phase = [], threading.Event(), ["idle"]
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                d = json.loads(r.stdout)
+                g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else d[0]
+                pw = g["power"]["socket_power"]
+                clk = [v["clk"]["value"] for k_, v in g["clock"].items()
+                       if k_.startswith("gfx") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                samples.append((phase[0], float(pw["value"]), statistics.mean(clk)))
+            except Exception as e:          # a sample that cannot be read is skipped, and said so
+                log(f"[power] sample skipped: {e}")
+            time.sleep(0.25)
+
+    w = make_config(5)
+    up = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, do = up(w.q()), up(w.k()), up(w.v()), up(w.do())
+    cu = torch.as_tensor(w.cu_seqlens, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.tq), dtype=torch.float32, device=dev)
+    dq = torch.empty((w.tq, w.hq, w.d), dtype=torch.float32, device=dev)
+    dk = torch.empty((w.tkv, w.hkv, w.d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    pairs = int(api.schedule(cu, w.chunks, 0, w.total, 128, 64)["counters"][3].item())
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    legs = (("fwd", lambda: api.attn_fwd(q, k, v, cu, w.chunks, 0, w.total, w.scale, out=o, lse=lse),
+             4.0 * w.d * w.hq * pairs),
+            ("bwd", lambda: api.attn_bwd(q, k, v, o, lse, do, cu, w.chunks, 0, w.total, w.scale, dq=dq, dk=dk, dv=dv),
+             10.0 * w.d * w.hq * pairs),
+            ("gemm_bf16_8192", lambda: torch.matmul(a, b), 2.0 * 8192 ** 3))
+    for _, fn, _ in legs:
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(1.0)
+    result = {"study": "power", "workload": w.name, "phases": {}}
+    for name, fn, flop in legs:
+        phase[0] = name
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n, t0 = 0, time.time()
+        e0.record()
+        while time.time() - t0 < seconds:
+            for _ in range(4):
+                fn()
+            n += 4
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        result["phases"][name] = {"calls": n, "ms_per_call": round(ms, 4),
+                                  "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                                  "frac_of_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[power] {name}: {n} calls, {ms:.3f} ms each")
+        phase[0] = "idle"
+        time.sleep(1.0)
+    stop.set()
+    th.join()
+    for name in list(result["phases"]) + ["idle"]:
+        sel = [(pw, c) for ph, pw, c in samples if ph == name]
+        if sel:
+            result["phases"].setdefault(name, {}).update({
+                "samples": len(sel), "board_power_w_median": statistics.median(x for x, _ in sel),
+                "board_power_w_max": max(x for x, _ in sel), "gfx_clock_mhz_median": round(statistics.median(c for _, c in sel), 1)})
     print(json.dumps(result), flush=True)
 
 

@@ -32,11 +32,15 @@
 
 namespace docmask {
 
-// Rescale threshold (log2 units): the running row maximum used as the softmax
-// reference is only raised when a tile's maximum exceeds it by more than this,
-// so exp2 arguments stay <= kRescaleTau and most tiles skip the O rescale.
-// The result is the same after the final normalisation by the row sum.
-constexpr float kRescaleTau = 8.f;
+// Softmax reference.  A tile's exponentials are first formed against the
+// running reference m (no tile maximum is taken); the tile is accepted when no
+// lane's sum of them exceeds kAcceptSum, so every accepted value is at most
+// 2^15 (rounded to bf16 with its usual 8-bit precision, far from fp32
+// overflow in O and the row sum).  Otherwise (and while some row of the wave
+// has no reference yet) the tile's maximum is taken, the reference raised to
+// it, O and the sum rescaled, and the exponentials formed again.  Any
+// reference gives the same result after the final division by the row sum.
+constexpr float kAcceptSum = 32768.f;
 
 template <int D, int RB, int HB>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
@@ -153,16 +157,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   // S^T = K Q^T for the two 32-key blocks of the tile held in K buffer kb_
   auto compute_s = [&](const uint16_t* kl, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
-    // the two 32-key blocks alternate, so consecutive MFMAs are independent
+    constexpr int NT = 2 * NKS, PFS = 4;
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&kl[(32 * kb + ln) * KSTR + 16 * s + 8 * hh]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
-      }
+    bf16x8 op[NT];
+    auto load = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      op[i] = *reinterpret_cast<const bf16x8*>(&kl[(32 * (i % 2) + ln) * KSTR + 16 * (i / 2) + 8 * hh]);
+    };
+    static_for<PFS>([&](auto ic) __attribute__((always_inline)) { load(ic); });
+    static_for<NT>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + PFS < NT) load(std::integral_constant<int, i + PFS>{});
+      sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[i / 2], sacc[i % 2], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // Pipeline over the n tiles (index u = kt - kt_lo): K tile u lives in
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (n > 0) {
     issue_k(kt_lo, k_lds[0]);
     issue_v(kt_lo, v_lds[0]);
-    issue_k(min(kt_lo + 1, kt_hi - 1), k_lds[1]);
+    if (n > 1) issue_k(kt_lo + 1, k_lds[1]);
   }
   // the first tiles are in flight while the Q operands load
 #pragma unroll
@@ -197,10 +206,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     constexpr bool has_next = decltype(has_next_c)::value;
     const int kt = kt_lo + u;
     if (has_next) {
-      // K tile u + 2 (the last tile again near the end) into the buffer K tile u
-      // left, V tile u + 1 into the one V tile u - 1 left; in flight during this
-      // tile's math
-      issue_k(min(kt + 2, kt_hi - 1), k_lds[u & 1]);
+      // K tile u + 2 (if any) into the buffer K tile u left, V tile u + 1 into
+      // the one V tile u - 1 left; in flight during this tile's math
+      if (kt + 2 < kt_hi) issue_k(kt + 2, k_lds[u & 1]);
       issue_v(kt + 1, v_lds[(u + 1) & 1]);
     }
 
@@ -216,36 +224,45 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
           if (rel > (unsigned)a_w) s_cur[kb][r] = -INFINITY;
         }
     }
-    // online softmax (base 2) with a lazily raised reference
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
-    mx = pair_max32(mx);
-    const float m_tile = mx * p.scale_log2;
-    if (__any(m_tile > m_run + kRescaleTau)) {       // wave-uniform branch
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // online softmax (base 2) against the running reference (see kAcceptSum)
     float rs = 0.f;
     bf16x8 pf[4];
+    auto exps = [&](float m_use) __attribute__((always_inline)) {
+      float r_ = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], p.scale_log2, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r + 1], p.scale_log2, -m_use));
-        rs += e0 + e1;
-        const bf16x2 two = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
-        pf[2 * kb + (r >> 3)][r & 7] = two[0];
-        pf[2 * kb + (r >> 3)][(r & 7) + 1] = two[1];
+        for (int r = 0; r < 16; r += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], p.scale_log2, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r + 1], p.scale_log2, -m_use));
+          r_ += e0 + e1;
+          const bf16x2 two = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
+          pf[2 * kb + (r >> 3)][r & 7] = two[0];
+          pf[2 * kb + (r >> 3)][(r & 7) + 1] = two[1];
+        }
+      return r_;
+    };
+    bool redo = true;
+    if (!__any(m_run == -INFINITY)) {
+      rs = exps(m_run);
+      redo = __any(rs > kAcceptSum);
+    }
+    if (redo) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
+      const float m_new = fmaxf(m_run, pair_max32(mx) * p.scale_log2);
+      if (__any(m_new > m_run)) {
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
       }
+      rs = exps(m_run == -INFINITY ? 0.f : m_run);
+    }
     l_run += rs;
     // S of the next tile, into the registers this tile's softmax has just
     // read; those MFMAs and this tile's PV run back to back, at raised wave

@@ -256,6 +256,7 @@ def test_one_million_tokens_document_tails():
 
 
 
+@pytest.mark.timeout(900)
 def test_cp_rank_split_backward():
     """Rank 3 of CP = 8 run as a ring rank runs it: per-(chunk, 8192-key block)
     backward calls with the merged O and LSE, dQ shares accumulated, Delta
@@ -302,3 +303,33 @@ def test_cp_rank_split_backward():
     wq, _, _ = oracle.attention_backward(f64(q[sel]), f64(k), f64(v), f64(do[sel]), cu,
                                          [(int(pos[r]), 1) for r in sel], w.kv_lo, w.kv_hi, w.scale)
     assert_close(dq1.cpu().numpy()[sel], wq, O_TOL, "single-call dQ vs oracle")
+    # dK / dV of sampled keys against the oracle: 64-key runs at the start of
+    # each chunk's document (attended by every row of the chunk, the longest
+    # walks over query blocks) and at each chunk's end.  On this rank a key is
+    # attended only by the rank's rows of its own document at or after it, so
+    # the sub-problem (those rows; keys from the document start to the chunk
+    # end) is exact for the sampled keys.  One KV-head group each.
+    dk1n, dv1n = dk1.cpu().numpy(), dv1.cpu().numpy()
+    g = w.hq // w.hkv
+    row0 = 0
+    for ci, (gs, n) in enumerate(w.chunks):
+        d = int(np.searchsorted(cu, gs, side="right") - 1)
+        ds, de = int(cu[d]), int(cu[d + 1])
+        assert gs + n <= de, "the sampled keys' attending rows are the chunk's own"
+        for j0 in (ds, gs + n - 64):
+            kvh = (ci + j0) % w.hkv
+            heads = np.arange(kvh * g, (kvh + 1) * g)
+            r0 = max(j0, gs)
+            rows = slice(row0 + r0 - gs, row0 + n)
+            keys = np.arange(ds, gs + n)
+            tag = f"CP rank chunk {gs}: keys [{j0},{j0 + 64}) kv head {kvh}, {gs + n - r0} attending rows"
+            print(f"[cp bwd] {tag}", flush=True)
+            (_, wk, wv), secs = timed_s(lambda: _oracle_backward_by_head(
+                f64(q[rows][:, heads]), f64(k[keys][:, kvh:kvh + 1]), f64(v[keys][:, kvh:kvh + 1]),
+                f64(do[rows][:, heads]), cu, [(r0, gs + n - r0)], ds, gs + n, w.scale, tag))
+            ek = assert_close(dk1n[j0:j0 + 64, kvh:kvh + 1], wk[j0 - ds:j0 - ds + 64], O_TOL, f"{tag} dK")
+            ev = assert_close(dv1n[j0:j0 + 64, kvh:kvh + 1], wv[j0 - ds:j0 - ds + 64], O_TOL, f"{tag} dV")
+            record(config=3, seed=w.seed, check=f"backward over the rank's whole KV range, 64 keys at {j0}",
+                   compared=f"dK, dV of 64 keys (KV head {kvh}, {g} query heads, {gs + n - r0} attending rows)",
+                   err_dK=ek, err_dV=ev, oracle_s=round(secs, 2), cores=host_cores())
+        row0 += n
