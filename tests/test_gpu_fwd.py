@@ -281,3 +281,48 @@ def test_one_million_tokens_sampled_rows():
                                               [(int(r), 1) for r in rows], 0, w.total, w.scale)
     assert_close(bf16_to_np(o[torch.as_tensor(rows, device="cuda")]), want_o, O_TOL, "2^20 O")
     assert_close(lse[:, torch.as_tensor(rows, device="cuda")].cpu().numpy(), want_l, LSE_TOL, "2^20 LSE")
+
+
+def _trend_inputs(lengths, slopes, hq, hkv, d, seed):
+    """Q rows all close to one direction v and K rows drifting along v with the
+    key's position in its document (slope per key, in units of v), plus noise:
+    a row's scores then grow (slope > 0) or shrink (slope < 0) steadily along
+    its document.  bf16 bit patterns, like the seeded generator's."""
+    from document_masked_attention_amd.workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    total = sum(lengths)
+    v = rng.standard_normal(d).astype(np.float32)
+    v /= np.linalg.norm(v)
+    q = 0.3 * rng.standard_normal((total, hq, d)).astype(np.float32) + 4.0 * v
+    k = 0.5 * rng.standard_normal((total, hkv, d)).astype(np.float32)
+    pos = 0
+    for n, slope in zip(lengths, slopes):
+        k[pos:pos + n] += (slope * np.arange(n, dtype=np.float32))[:, None, None] * v
+        pos += n
+    vv = rng.standard_normal((total, hkv, d)).astype(np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(vv)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_rising_along_the_document(d):
+    """The forward forms a tile's exponentials against the running reference and
+    takes the tile maximum (raising the reference, rescaling O) only when some
+    lane's sum exceeds 2^15 or a row has no reference yet.  Steeply rising
+    scores force that on nearly every tile (first document), gently rising
+    ones after many accepted tiles (second), falling ones never after the
+    first tile (third, exponentials underflowing to zero); all against the
+    oracle, every row."""
+    lengths, slopes = [700, 1500, 900], [0.9, 0.02, -0.05]
+    hq, hkv = 8, 2
+    q, k, v = _trend_inputs(lengths, slopes, hq, hkv, d, 50 + d)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total = int(cu[-1])
+    scale = 1.0 / math.sqrt(d)
+    print(f"[fwd] rising scores d={d} lengths={lengths} slopes={slopes}", flush=True)
+    o, lse = api.attn_fwd(to_dev(q), to_dev(k), to_dev(v), cu, [(0, total)], 0, total, scale)
+    torch.cuda.synchronize()
+    want_o, want_l = oracle.attention_forward(f64(q), f64(k), f64(v), cu, [(0, total)], 0, total, scale)
+    # the steep document's scores span hundreds of natural-log units along a row
+    assert want_l[:, cu[1] - 1].min() > want_l[:, 0].max() + 100
+    assert_close(bf16_to_np(o), want_o, O_TOL, "rising scores O")
+    assert_close(lse.cpu().numpy(), want_l, LSE_TOL, "rising scores LSE")
