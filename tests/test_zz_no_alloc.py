@@ -44,3 +44,50 @@ def test_noalloc_forward_two_calls_second_smaller():
     _compare(big, "first call (larger)")
     _compare(small, "second call (smaller)")
     _compare(big, "third call (larger again)")
+
+
+def test_noalloc_forward_graph_replays_after_other_calls():
+    """Captured in a HIP graph (the callers this entry point is for), with an
+    eager call on another problem between replays overwriting the shared
+    scratch: every replay gives the eager result bit for bit, because each call
+    writes every scratch region it reads before reading it."""
+    rng = np.random.default_rng(43)
+    w = custom_workload(43, random_lengths(rng, 3000, 900, p_one=0.05), 8, 2, 128)
+    other = custom_workload(44, random_lengths(rng, 5000, 2500, p_one=0.05), 16, 4, 64,
+                            chunks=[(0, 2000), (3000, 2000)], kv_lo=0, kv_hi=5000)
+    print(f"[noalloc graph] T={w.total} h={w.hq}/{w.hkv} d={w.d}; other T={other.total} "
+          f"h={other.hq}/{other.hkv} d={other.d}", flush=True)
+    q, k, v = to_dev(w.q()), to_dev(w.k()), to_dev(w.v())
+    cu = torch.as_tensor(w.cu_seqlens, dtype=torch.int32, device="cuda")
+    oq, ok_, ov = to_dev(other.q()), to_dev(other.k()), to_dev(other.v())
+    ocu = torch.as_tensor(other.cu_seqlens, dtype=torch.int32, device="cuda")
+    o = torch.empty((w.tq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.hq, w.tq), dtype=torch.float32, device="cuda")
+    o2 = torch.empty((other.tq, other.hq, other.d), dtype=torch.bfloat16, device="cuda")
+    lse2 = torch.empty((other.hq, other.tq), dtype=torch.float32, device="cuda")
+
+    def run():
+        api.attn_fwd_noalloc(q, k, v, cu, w.chunks, w.kv_lo, w.kv_hi, w.scale, out=o, lse=lse)
+
+    run()
+    torch.cuda.synchronize()
+    ref_o, ref_l = o.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        api.attn_fwd_noalloc(oq, ok_, ov, ocu, other.chunks, other.kv_lo, other.kv_hi, other.scale, out=o2, lse=lse2)
+        o.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}: O differs"
+        assert torch.equal(lse, ref_l), f"replay {rep}: LSE differs"
