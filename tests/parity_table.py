@@ -1,7 +1,7 @@
 """Markdown table of the measured parity errors that the GPU tests record.
 
-    DOCMASK_PARITY_LOG=gpurun_out/parity_rows.jsonl python -m pytest tests -m gpu
-    python tests/parity_table.py gpurun_out/parity_rows.jsonl > profiles/parity_errors_all_workloads.md
+    DOCMASK_PARITY_LOG=/tmp/parity_rows.jsonl python -m pytest tests -m gpu
+    python tests/parity_table.py /tmp/parity_rows.jsonl > profiles/parity_errors_all_workloads.md
 
 One row per full-size check (workload, seed, what was compared): max abs
 error of O, LSE, dQ, dK, dV against the float64 oracle, the GPU call's time,
