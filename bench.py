@@ -212,7 +212,8 @@ def main():
                     help="instead of the step benchmark: 'sharding' times every CP rank's forward under "
                          "per-sequence, per-document and Algorithm 1 sharding; 'length' times forward and "
                          "backward of one GPU's sequence from 32K to 1M tokens; 'power' samples board power and "
-                         "clocks (amd-smi) while the forward, the backward and a bf16 GEMM run back to back")
+                         "clocks (amd-smi) while the forward, the backward, a bf16 GEMM and the matrix-core probe "
+                         "run back to back")
     ap.add_argument("--cp", type=int, default=8, help="CP size of the sharding study")
     ap.add_argument("--cp-backward", action="store_true",
                     help="also time the CP rank's backward (per-block calls vs one call); off by default so that "
@@ -410,9 +411,12 @@ def main():
 
 def study_power(seconds: float = 4.0):
     """Board power and GFX clocks (amd-smi, sampled about every 0.3 s) while
-    the step's forward, its backward and, as a reference of what the chip
-    sustains on pure matrix work, a bf16 8192^3 GEMM (torch.matmul) each run
-    back to back for `seconds`; one JSON line with the medians per phase."""
+    the step's forward, its backward and, as references of what the chip
+    sustains on pure matrix work, a bf16 8192^3 GEMM (torch.matmul) and the
+    library's matrix-core probe (back-to-back v_mfma_f32_32x32x16_bf16 on
+    operands in registers, no memory traffic; N(0, 1) bf16 operands, and all
+    zeros as a control for data-dependent power) each run back to back for
+    `seconds`; one JSON line with the medians per phase."""
     import statistics
     import subprocess
     import threading
@@ -450,11 +454,18 @@ def study_power(seconds: float = 4.0):
     pairs = int(api.schedule(cu, w.chunks, 0, w.total, 128, 64)["counters"][3].item())
     a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
     b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    probe_ops = torch.randn(1 << 20, device=dev, dtype=torch.bfloat16)
+    probe_zero = torch.zeros(1 << 20, device=dev, dtype=torch.bfloat16)
+    probe_wg, probe_iters = 2048, 1024         # 8 workgroups per CU over the run, 2 resident
+    probe_out = torch.empty(256 * probe_wg, device=dev, dtype=torch.float32)
+    probe_flop = float(api.PROBE_FLOP_PER_WAVE_ITER) * probe_iters * 4 * probe_wg
     legs = (("fwd", lambda: api.attn_fwd(q, k, v, cu, w.chunks, 0, w.total, w.scale, out=o, lse=lse),
              4.0 * w.d * w.hq * pairs),
             ("bwd", lambda: api.attn_bwd(q, k, v, o, lse, do, cu, w.chunks, 0, w.total, w.scale, dq=dq, dk=dk, dv=dv),
              10.0 * w.d * w.hq * pairs),
-            ("gemm_bf16_8192", lambda: torch.matmul(a, b), 2.0 * 8192 ** 3))
+            ("gemm_bf16_8192", lambda: torch.matmul(a, b), 2.0 * 8192 ** 3),
+            ("mfma_probe_randn", lambda: api.mfma_probe(probe_ops, probe_wg, probe_iters, out=probe_out), probe_flop),
+            ("mfma_probe_zero", lambda: api.mfma_probe(probe_zero, probe_wg, probe_iters, out=probe_out), probe_flop))
     for _, fn, _ in legs:
         fn()
     torch.cuda.synchronize()

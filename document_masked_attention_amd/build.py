@@ -24,7 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdocmask.so")
-SOURCES = ["abi.hip", "sched.hip", "fwd.hip", "bwd.hip", "merge.hip", "timing.hip", "exchange.hip", "plan.hip"]
+SOURCES = ["abi.hip", "sched.hip", "fwd.hip", "bwd.hip", "merge.hip", "timing.hip", "exchange.hip", "plan.hip",
+           "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",

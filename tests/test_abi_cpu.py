@@ -148,6 +148,18 @@ def test_timing_controls(lib):
     assert lib.docmask_timing_read(0, None, ctypes.byref(n)) == api.EINVAL
 
 
+def test_mfma_probe_validation(lib):
+    probe = lib.docmask_mfma_probe
+    assert probe(None, 1024, 1, 1, FAKE, None) == api.EINVAL
+    assert probe(FAKE, 1024, 1, 1, None, None) == api.EINVAL
+    assert probe(MIS, 1024, 1, 1, FAKE, None) == api.EINVAL            # operands not 16-byte aligned
+    assert probe(FAKE, 1024, 1, 1, FAKE + 2, None) == api.EINVAL       # out not 4-byte aligned
+    assert probe(FAKE, 120, 1, 1, FAKE, None) == api.EINVAL            # fewer than 128 values
+    assert probe(FAKE, 1028, 1, 1, FAKE, None) == api.EINVAL           # not a multiple of 8
+    assert probe(FAKE, 1024, 0, 1, FAKE, None) == api.EINVAL
+    assert probe(FAKE, 1024, 1, -1, FAKE, None) == api.EINVAL
+
+
 def _copy(lib, maps=((0, 0, 4),), src_k=FAKE, src_v=FAKE, dst_k=FAKE, dst_v=FAKE, src_rows=10, dst_rows=10,
           row_bytes=64, zero=0):
     arr, n = api._maps_arr(list(maps))
