@@ -332,7 +332,7 @@ const char* docmask_kernel_class_name(int kernel_class);
 
 /* Matrix-core rate probe (instrumentation; defines no attention operation).
  * Measures what the matrix cores sustain on given bf16 data: n_workgroups
- * workgroups of 4 waves (two workgroups per compute unit) each run `iters`
+ * workgroups of 4 waves (at most two resident per compute unit) each run `iters`
  * iterations of 16 v_mfma_f32_32x32x16_bf16 -- the instruction of the
  * attention kernels -- on operands held in registers, with no other memory
  * traffic.  Lane gl (global thread index) loads its 8 A and 8 B operand
