@@ -26,8 +26,8 @@ ACCUMULATE_DQ = 1
 DELTA_READY = 2
 MAX_CHUNKS = 256
 (KERNEL_SCHEDULE, KERNEL_FWD, KERNEL_DELTA, KERNEL_DKDV, KERNEL_DQ, KERNEL_MERGE,
- KERNEL_CONVERT, KERNEL_COPY) = range(8)
-N_KERNEL_CLASSES = 8
+ KERNEL_CONVERT, KERNEL_COPY, KERNEL_HEAD) = range(9)
+N_KERNEL_CLASSES = 9
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32

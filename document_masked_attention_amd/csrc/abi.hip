@@ -378,7 +378,7 @@ int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o,
   bp.accumulate_dq = (flags & DOCMASK_ACCUMULATE_DQ) != 0;
   bp.scale = softmax_scale;
   bp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-  return hip_status(launch_bwd(bp, d, (flags & DOCMASK_DELTA_READY) != 0, stream));
+  return hip_status(launch_bwd(bp, sp.ch, d, (flags & DOCMASK_DELTA_READY) != 0, stream));
 }
 
 // o_parts (bf16) or o_parts32 (float32): exactly one holds the partials

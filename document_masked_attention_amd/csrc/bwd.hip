@@ -8,7 +8,9 @@
 //   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 // with dK and dV summed over the query heads of each KV group.
 //
-// Two kernels, both deterministic (no atomics), launched in this order:
+// Three kernels, all deterministic (no atomics), launched in this order (the
+// first two leave out each document's first kBwdHead x kBwdHead positions,
+// which the third computes in fp32):
 //
 // * dq_kernel, query-major, shaped like the forward.  Work item = (query tile,
 //   KV head, block of query heads), 4 waves, two workgroups per CU; each
@@ -29,6 +31,8 @@
 //     dP = dO V^T,  dS = P (dP - Delta),  dK^T += Q^T dS
 //   (v_mfma_f32_32x32x16_bf16; Q^T and dO^T come from the row-major tiles
 //   through LDS transpose reads).
+// * head_kernel: the pairs ds <= j <= i < ds + kBwdHead of every document
+//   (ds its start) in fp32, added to dq, dk and dv (see there).
 #include "kernels.h"
 
 
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // Per-tile state, set at the start of each part: the tile's query-block
   // range, this lane's key, the walking direction over the query blocks.
   int tile = lead, qt_lo = 0, qt_flo = 0, qt_fhi = 0, qt_hi = 0, dir = -1;
-  int key_l = 0, key_g = 0, key_end = 0, n_units = 0, n_steps = 0;
+  int key_l = 0, key_g = 0, key_row0 = 0, key_end = 0, n_units = 0, n_steps = 0;
   bool key_ok = false, ragged = false;
   bf16x8 kf[NKS], vf[NKS];        // K and V rows of this lane's key as B operands: d = 16 s + 8 hh .. +8
   f32x16 dkacc[NMB], dvacc[NMB];
@@ -284,8 +288,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // pairs that are not allowed become -inf (P = 0).  Only units outside the
   // tile's FULL range need it; the caller branches on ui.masked.
   auto unit_mask = [&](const UnitInfo& ui, f32x16& sa) __attribute__((always_inline)) {
-    // allowed rows: key_g <= g_row0 + qr < key_end, qr < nrows
-    const int lo = key_g - ui.g_row0;
+    // rows this pass takes: key_row0 <= g_row0 + qr < key_end, qr < nrows
+    const int lo = key_row0 - ui.g_row0;
     const int hi = key_ok ? min(key_end - ui.g_row0, ui.nrows) : lo;
     const unsigned span = (unsigned)max(hi - lo, 0);
     mfma_v_settle();
@@ -441,6 +445,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     key_ok = key_l < tkv;
     key_g = p.kv_lo + key_l;
     key_end = key_ok ? doc_end(p.cu, p.n_docs, key_g) : key_g;
+    // a key among its document's first kBwdHead positions leaves the rows
+    // among those positions to the head pass (fp32); its other rows are here
+    key_row0 = key_g;
+    if (key_ok) {
+      const int ds = doc_start(p.cu, p.n_docs, key_g);
+      if (key_g - ds < kBwdHead) key_row0 = ds + kBwdHead;
+    }
     ragged = (tile + 1) * BK > tkv;
     {
       const int kl = min(key_l, tkv - 1);               // padding keys: any finite row, masked below
@@ -480,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       finish(1, in0, in1);
       // the key's document end and the K / V operands are in registers before
       // any later loads are in flight
-      asm volatile("" ::"v"(key_end));
+      asm volatile("" ::"v"(key_end), "v"(key_row0));
 #pragma unroll
       for (int s = 0; s < NKS; ++s) asm volatile("" ::"a"(kf[s]), "a"(vf[s]));
       __syncthreads();
@@ -641,8 +652,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   int a_lo = 0x40000000, a_w = 0;
   float lse2 = INFINITY, dlt = 0.f;
   if (row_ok) {
-    const int lo = max(doc_start(p.cu, p.n_docs, gi), p.kv_lo), hi = min(gi, p.kv_hi - 1);
-    if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
+    // a row among its document's first kBwdHead positions attends only keys
+    // among them: all of its pairs belong to the head pass (fp32)
+    const int ds = doc_start(p.cu, p.n_docs, gi);
+    const int lo = max(ds, p.kv_lo), hi = min(gi, p.kv_hi - 1);
+    if (hi >= lo && gi - ds >= kBwdHead) { a_lo = lo; a_w = hi - lo; }
     const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr];
     lse2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
     if (p.delta_ready) dlt = p.delta[(size_t)head * p.tq + l_row0 + qr];
@@ -778,6 +792,285 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------ head pass
+// The pairs (i, j) with ds <= j <= i < ds + kBwdHead of every document (ds its
+// start) -- the rows with the fewest keys, whose P and dS are the largest --
+// in fp32 throughout: the two kernels above leave them out, because rounding
+// P and dS to the bf16 matrix-core operands costs the most there.  These rows
+// also take their Delta from the pass's own P and dP when all their keys are
+// in the call's KV range (the bf16 O that the other rows' Delta is formed
+// from is least accurate for rows with few keys).  Workgroup =
+// (document, KV head); it adds the pairs' dQ shares of the group's query heads
+// into dq and their dK and dV (summed over those heads) into dk and dv, after
+// both kernels have written them.  Only the pairs of this call count: rows in
+// its chunks, keys in [kv_lo, kv_hi).  Disjoint outputs per workgroup: the
+// result does not depend on the order in which workgroups run.
+template <int D>
+__global__ __launch_bounds__(256) void head_kernel(BwdParams p, ChunkTable ch) {
+  constexpr int H = kBwdHead;
+  constexpr int DS = D + 4;             // LDS row stride (floats): 16-byte row reads of 16 rows on distinct banks
+  constexpr int DG = D / 8;             // 8-wide d groups; 256 % DG == 0, so a thread keeps its d group
+  constexpr int NT = (H * DG + 255) / 256;   // (row or key, d group) tasks per thread
+  constexpr int NKS = D / 16;
+  static_assert(H == 32 || H == 64, "head block of one or three 32 x 32 MFMA tiles");
+  constexpr int NTILE = H == 32 ? 1 : 3;
+  __shared__ __attribute__((aligned(16))) float ks[H][DS], qs[H][DS], dos[H][DS];
+  __shared__ float ps[H][H + 1], dss[H][H + 1];
+  __shared__ int rl[H];                 // local query row of head position t, -1 if not a row of this call
+  __shared__ float lse2[H], dlt[H];
+
+  if (p.err[0]) return;
+  const int doc = blockIdx.x / p.hkv, kvh = blockIdx.x % p.hkv;
+  const int a = p.cu[doc], b = p.cu[doc + 1];
+  const int k0 = max(a, p.kv_lo), he = min(b, a + H), k1 = min(he, p.kv_hi);
+  if (k1 <= k0) return;                 // no head key in this call's KV range
+  const int nk = k1 - k0, nr = he - k0; // head keys [k0, k1); rows [k0, he) (a row before k0 has no such key)
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int dg0 = 8 * (tid % DG);       // this thread's d group
+
+  if (tid < H) {
+    int loc = -1;
+    if (tid < nr) {
+      const int g = k0 + tid;
+      int off = 0;
+      for (int c = 0; c < ch.n; ++c) {
+        if (g >= ch.g_start[c] && g < ch.g_start[c] + ch.len[c]) { loc = off + g - ch.g_start[c]; break; }
+        off += ch.len[c];
+      }
+    }
+    rl[tid] = loc;
+  }
+  // K rows of the head keys (float, for dQ)
+  for (int t = tid; t < H * DG; t += 256) {
+    const int c = t / DG;
+    float kf[8] = {};
+    if (c < nk) {
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(p.k + ((size_t)(k0 + c - p.kv_lo) * p.hkv + kvh) * D + dg0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[e] = (float)kb[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ks[c][dg0 + e] = kf[e];
+  }
+  __syncthreads();
+  bool any_row = false;
+  for (int r = 0; r < nr; ++r) any_row |= rl[r] >= 0;
+  if (!any_row) return;                 // no head row among this call's query rows
+
+  // S and dP by v_mfma_f32_32x32x16_bf16 (exact bf16 products, fp32 sums):
+  // wave 0 takes the 32 x 32 tile (rows 0-31, keys 0-31), and for H = 64
+  // waves 1 and 2 the tiles (32-63, 0-31) and (32-63, 32-63); lane l holds
+  // key column l % 32 of its tile.  The K and V operands of this lane's key
+  // stay in registers for all heads.
+  const int rt = wave == 0 ? 0 : 1, kt = wave == 2 ? 1 : 0;
+  const int kcol = 32 * kt + l32;
+  bf16x8 kop[NKS], vop[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    kop[s] = bf16x8{};
+    vop[s] = bf16x8{};
+    if (wave < NTILE && kcol < nk) {
+      const size_t off = ((size_t)(k0 + kcol - p.kv_lo) * p.hkv + kvh) * D + 16 * s + 8 * hh;
+      kop[s] = *reinterpret_cast<const bf16x8*>(p.k + off);
+      vop[s] = *reinterpret_cast<const bf16x8*>(p.v + off);
+    }
+  }
+
+  float dka[NT][8], dva[NT][8];         // dK, dV of keys (tid + 256 i) / DG, summed over the group's heads
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { dka[i][e] = 0.f; dva[i][e] = 0.f; }
+
+  // Q and dO of this thread's fill tasks (row (tid + 256 i) / DG, its d
+  // group), LSE and Delta of head position tid: loaded one head ahead, so
+  // that their latency overlaps the previous head's work
+  bf16x8 pq[NT], pd[NT];
+  float plse = -INFINITY, pdlt = 0.f;
+  auto prefetch = [&](int head) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = tid + 256 * i, r = min(t / DG, H - 1);
+      const int lr = r < nr ? rl[r] : -1;
+      pq[i] = bf16x8{};
+      pd[i] = bf16x8{};
+      if (lr >= 0 && t < H * DG) {
+        const size_t off = ((size_t)lr * p.hq + head) * D + dg0;
+        pq[i] = *reinterpret_cast<const bf16x8*>(p.q + off);
+        pd[i] = *reinterpret_cast<const bf16x8*>(p.d_o + off);
+      }
+    }
+    if (tid < H) {
+      const int lr = tid < nr ? rl[tid] : -1;
+      plse = -INFINITY;
+      pdlt = 0.f;
+      if (lr >= 0) {
+        plse = p.lse[(size_t)head * p.tq + lr];
+        pdlt = p.delta[(size_t)head * p.tq + lr];
+      }
+    }
+  };
+  prefetch(kvh * p.group);
+  for (int hs = 0; hs < p.group; ++hs) {
+    const int head = kvh * p.group + hs;
+    // this head's Q and dO rows (float), LSE (base 2) and Delta into LDS
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = tid + 256 * i;
+      if (t < H * DG) {
+        const int r = t / DG;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { qs[r][dg0 + e] = (float)pq[i][e]; dos[r][dg0 + e] = (float)pd[i][e]; }
+      }
+    }
+    if (tid < H) {
+      lse2[tid] = plse == -INFINITY ? INFINITY : plse * kLog2e;
+      dlt[tid] = pdlt;
+    }
+    __syncthreads();
+    if (hs + 1 < p.group) prefetch(head + 1);
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    if (wave < NTILE) {
+      // A operands: this lane's row of the tile from the LDS rows (bf16
+      // values, so the conversion back is exact); rows past the head are zero
+      const int row = 32 * rt + l32;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        bf16x8 qa = bf16x8{}, da = bf16x8{};
+        if (row < H) {
+          const float* qr_ = &qs[row][16 * s + 8 * hh];
+          const float* dr_ = &dos[row][16 * s + 8 * hh];
+          qa = cvt8(qr_[0], qr_[1], qr_[2], qr_[3], qr_[4], qr_[5], qr_[6], qr_[7]);
+          da = cvt8(dr_[0], dr_[1], dr_[2], dr_[3], dr_[4], dr_[5], dr_[6], dr_[7]);
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vop[s], pacc, 0, 0, 0);
+      }
+    }
+    if (wave < NTILE) {
+      // element e of the tiles: row 32 rt + 8 (e / 4) + 4 hh + e % 4, key kcol;
+      // pairs outside the head triangle (key after row), or of rows not in
+      // this call, get P = 0
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 32 * rt + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (r >= H || kcol >= H) continue;
+        float pr = 0.f;
+        if (r < nr && kcol < nk && kcol <= r && rl[r] >= 0)
+          pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], p.scale_log2, -lse2[r]));
+        ps[r][kcol] = pr;
+        dss[r][kcol] = pacc[e];         // dP for now
+      }
+    } else if (NTILE == 3 && wave == 3) {
+      // wave 3: the tile (rows 0-31, keys 32-63) lies above the diagonal
+      for (int t = lane; t < 32 * (H - 32); t += 64) {
+        const int r = t / (H - 32), c = 32 + t % (H - 32);
+        ps[r][c] = 0.f;
+        dss[r][c] = 0.f;
+      }
+    }
+    __syncthreads();
+    // Delta of a head row whose keys all lie in this call's KV range: the
+    // sum over them of P dP (= dO . O with O in fp32, not the bf16 O the
+    // other rows' Delta comes from)
+    if (tid < nr && rl[tid] >= 0 && a >= p.kv_lo && k0 + tid < p.kv_hi) {
+      float acc = 0.f;
+      for (int c = 0; c <= tid; ++c) acc = __builtin_fmaf(ps[tid][c], dss[tid][c], acc);
+      dlt[tid] = acc;
+    }
+    __syncthreads();
+    for (int t = tid; t < H * H; t += 256) {
+      const int r = t / H, c = t % H;
+      dss[r][c] = ps[r][c] * (dss[r][c] - dlt[r]);
+    }
+    __syncthreads();
+    // dQ of the head rows (tid + 256 i) / DG: scale * sum_c dS[r][c] k_c,
+    // added to dq (its old values load while the dK / dV sums run)
+    float acc[NT][8];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+    {
+      int rows_i[NT];                   // task rows, clamped (a clamped task's result is not written)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) rows_i[i] = min((tid + 256 * i) / DG, H - 1);
+#pragma unroll 4
+      for (int c = 0; c < nk; ++c) {
+        const f32x4 k0v = *reinterpret_cast<const f32x4*>(&ks[c][dg0]);
+        const f32x4 k1v = *reinterpret_cast<const f32x4*>(&ks[c][dg0 + 4]);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const float w = dss[rows_i[i]][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[i][e] = __builtin_fmaf(w, k0v[e], acc[i][e]);
+            acc[i][4 + e] = __builtin_fmaf(w, k1v[e], acc[i][4 + e]);
+          }
+        }
+      }
+    }
+    float* dqp[NT];
+    float4 old[NT][2];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int r = (tid + 256 * i) / DG;
+      const int lr = r < nr ? rl[r] : -1;   // r < nr <= H: not a clamped task
+      dqp[i] = lr >= 0 ? p.dq + ((size_t)lr * p.hq + head) * D + dg0 : nullptr;
+      if (dqp[i]) {
+        old[i][0] = *reinterpret_cast<const float4*>(dqp[i]);
+        old[i][1] = *reinterpret_cast<const float4*>(dqp[i] + 4);
+      }
+    }
+    // dK and dV of the head keys (tid + 256 i) / DG: sums over the head rows
+    {
+      int keys_i[NT];                   // task keys, clamped (a clamped task's result is not written)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) keys_i[i] = min((tid + 256 * i) / DG, H - 1);
+#pragma unroll 4
+      for (int r = 0; r < nr; ++r) {
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qs[r][dg0]);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qs[r][dg0 + 4]);
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(&dos[r][dg0]);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&dos[r][dg0 + 4]);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const float w = dss[r][keys_i[i]], pw = ps[r][keys_i[i]];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dka[i][e] = __builtin_fmaf(w, q0[e], dka[i][e]);
+            dka[i][4 + e] = __builtin_fmaf(w, q1[e], dka[i][4 + e]);
+            dva[i][e] = __builtin_fmaf(pw, o0[e], dva[i][e]);
+            dva[i][4 + e] = __builtin_fmaf(pw, o1[e], dva[i][4 + e]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (!dqp[i]) continue;
+      const float4 n0 = make_float4(old[i][0].x + acc[i][0] * p.scale, old[i][0].y + acc[i][1] * p.scale,
+                                    old[i][0].z + acc[i][2] * p.scale, old[i][0].w + acc[i][3] * p.scale);
+      const float4 n1 = make_float4(old[i][1].x + acc[i][4] * p.scale, old[i][1].y + acc[i][5] * p.scale,
+                                    old[i][1].z + acc[i][6] * p.scale, old[i][1].w + acc[i][7] * p.scale);
+      *reinterpret_cast<float4*>(dqp[i]) = n0;
+      *reinterpret_cast<float4*>(dqp[i] + 4) = n1;
+    }
+    __syncthreads();                    // before the next head's rows overwrite qs, dos, ps, dss
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int c = (tid + 256 * i) / DG;
+    if (c >= nk) continue;              // c < nk <= H: not a clamped task
+    const size_t off = ((size_t)(k0 + c - p.kv_lo) * p.hkv + kvh) * D + dg0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p.dk[off + e] += dka[i][e] * p.scale;
+      p.dv[off + e] += dva[i][e];
+    }
+  }
+}
+
 // query heads per dQ work item: as many heads of the GQA group as divide it (<= 8)
 static int dq_heads_per_item(int group) {
   return (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
@@ -785,7 +1078,7 @@ static int dq_heads_per_item(int group) {
 
 int dq_rows_per_tile(int group) { return 32 * (4 / dq_heads_per_item(group)); }
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p, const ChunkTable& ch, int d, bool delta_ready, hipStream_t stream) {
   // dQ first: unless the caller supplied Delta, its work items compute and
   // store it, and the dK/dV kernel reads it
   const int hb = dq_heads_per_item(p.group);
@@ -814,6 +1107,14 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t s
     KernelTimer timer(KC_DKDV, stream);
     if (d == 128) hipLaunchKernelGGL((dkdv_kernel<128>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((dkdv_kernel<64>), grid, block, 0, stream, p);
+  }
+  // the head pass adds to what both kernels wrote
+  const long long nblk_h = (long long)p.n_docs * p.hkv;
+  if (nblk_q > 0 && nblk_h > 0) {
+    if (nblk_h > 0x7fffffffLL) return hipErrorInvalidValue;
+    KernelTimer timer(KC_HEAD, stream);
+    if (d == 128) hipLaunchKernelGGL((head_kernel<128>), dim3((unsigned)nblk_h), dim3(256), 0, stream, p, ch);
+    else hipLaunchKernelGGL((head_kernel<64>), dim3((unsigned)nblk_h), dim3(256), 0, stream, p, ch);
   }
   return hipGetLastError();
 }

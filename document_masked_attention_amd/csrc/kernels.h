@@ -80,6 +80,13 @@ constexpr int kFwdBK = 64;
 constexpr int kBwdBQ = 32;
 constexpr int kBwdBK = 128;
 constexpr int kDqBK = 64;
+// Positions per document start whose pairs the backward evaluates in fp32 (the
+// head pass): every allowed pair (i, j) with ds <= j <= i < ds + kBwdHead, ds
+// the document start.  Must stay below kDqBK and kBwdBK, so that no FULL
+// tile of either backward kernel holds such a pair (the kernels mask them
+// out on their masked path).
+constexpr int kBwdHead = 32;
+static_assert(kBwdHead < kDqBK && kBwdHead < kBwdBK, "head pairs only in masked tiles");
 
 hipError_t launch_schedule(const SchedParams& p, int32_t* lpt_q, int32_t* lpt_kv, int32_t* hist,
                            hipStream_t stream);
@@ -87,7 +94,7 @@ hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream);
 int fwd_rows_per_tile(int group);
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream);
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int d, bool delta_ready, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, const ChunkTable& ch, int d, bool delta_ready, hipStream_t stream);
 int dq_rows_per_tile(int group);
 hipError_t launch_copy_rows(const void* src_k, const void* src_v, void* dst_k, void* dst_v, int64_t dst_rows,
                             int64_t row_bytes, const docmask_rowmap* maps, int32_t n_maps, bool zero_gaps,

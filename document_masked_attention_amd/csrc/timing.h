@@ -19,7 +19,8 @@ enum KernelClass {
   KC_MERGE = 5,
   KC_CONVERT = 6,
   KC_COPY = 7,       // KV exchange row copies
-  KC_COUNT = 8
+  KC_HEAD = 8,       // backward head pass (fp32 pairs at document starts)
+  KC_COUNT = 9
 };
 
 bool timing_enabled();

@@ -134,6 +134,7 @@ const char* docmask_kernel_class_name(int kernel_class) {
     case KC_MERGE: return "merge_kernel";
     case KC_CONVERT: return "f32_to_bf16_kernel";
     case KC_COPY: return "copy_rows_kernel";
+    case KC_HEAD: return "head_kernel";
     default: return "unknown";
   }
 }

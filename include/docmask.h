@@ -176,7 +176,12 @@ int docmask_attn_fwd_f32out(const void* q, const void* k, const void* v, const i
  * forward's outputs over the full KV extent of the rows (the merged values
  * for split-KV).  Outputs are float32: dq [Tq][Hq][D], dk and dv
  * [Tkv][Hkv][D].  dq is overwritten unless flags has DOCMASK_ACCUMULATE_DQ;
- * Delta is recomputed unless flags has DOCMASK_DELTA_READY. */
+ * Delta is recomputed unless flags has DOCMASK_DELTA_READY.  Precision: the
+ * products run on bf16 matrix cores (P and dS rounded to bf16), except the
+ * pairs among each document's first 32 positions -- the rows with the fewest
+ * keys, whose P and dS are the largest -- which are computed in float32, with
+ * their rows' Delta taken from the float32 P and dP rather than from the bf16
+ * o when all their keys lie in [kv_lo, kv_hi). */
 int docmask_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* d_o, const int32_t* cu_seqlens_dev, int32_t n_docs,
                      const docmask_chunk* chunks, int32_t n_chunks, int32_t kv_lo, int32_t kv_hi,
@@ -324,7 +329,8 @@ enum {
   DOCMASK_KERNEL_MERGE = 5,
   DOCMASK_KERNEL_CONVERT = 6,
   DOCMASK_KERNEL_COPY = 7,      /* docmask_copy_rows */
-  DOCMASK_N_KERNEL_CLASSES = 8
+  DOCMASK_KERNEL_HEAD = 8,      /* the backward's fp32 pass over pairs at document starts */
+  DOCMASK_N_KERNEL_CLASSES = 9
 };
 int docmask_timing_enable(int enable);
 int docmask_timing_read(int kernel_class, double* total_ms, int64_t* launches);

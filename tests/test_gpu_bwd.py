@@ -228,6 +228,52 @@ def test_full_size_whole_long_documents(cfg, ranks):
                err_dQ=eq, err_dK=ek, err_dV=ev, gpu_ms=round(ms, 3), oracle_s=round(secs, 2), cores=host_cores())
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_full_size_every_document_tail_every_kv_head(cfg):
+    """Every document of the full-size workloads (canonical seeds), every KV
+    head: its last <= 256 rows and keys against the oracle sub-problem (exact
+    there), so every short document is checked whole -- the rows with the
+    fewest keys, whose P and dS are the largest, are where rounding them to
+    the bf16 matrix-core operands costs the most."""
+    from threadpoolctl import threadpool_limits
+    w = make_config(cfg)
+    print(f"[bwd] config {cfg} seed {w.seed}: generating inputs", flush=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    dq, dk, dv = _gpu_fwd_bwd(w, q, k, v, do)
+    cu = w.cu_seqlens
+    g = w.hq // w.hkv
+    jobs = [(doc, kvh) for doc in range(len(cu) - 1) for kvh in range(w.hkv)]
+
+    def one(job):
+        doc, kvh = job
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        t0 = b - min(b - a, 256)
+        heads = np.arange(kvh * g, (kvh + 1) * g)
+        wq, wk, wv = oracle.attention_backward(f64(q[t0:b][:, heads]), f64(k[a:b, kvh:kvh + 1]),
+                                               f64(v[a:b, kvh:kvh + 1]), f64(do[t0:b][:, heads]), cu,
+                                               [(t0, b - t0)], a, b, w.scale)
+        return (float(np.abs(dq[t0:b][:, heads] - wq).max()), float(np.abs(dk[t0:b, kvh:kvh + 1] - wk[t0 - a:]).max()),
+                float(np.abs(dv[t0:b, kvh:kvh + 1] - wv[t0 - a:]).max()))
+
+    errs, secs = timed_s(lambda: _map_oracle(one, jobs, threadpool_limits))
+    e = np.max(np.array(errs), axis=0)
+    print(f"[bwd] config {cfg}: {len(jobs)} (document, KV head) tails, max abs error dQ {e[0]:.2e} dK {e[1]:.2e} "
+          f"dV {e[2]:.2e} (oracle {secs:.1f} s)", flush=True)
+    record(config=cfg, seed=w.seed, check="backward, every document tail on every KV head",
+           compared=f"last <= 256 rows and keys of all {len(cu) - 1} documents x {w.hkv} KV-head groups",
+           err_dQ=e[0], err_dK=e[1], err_dV=e[2], oracle_s=round(secs, 2), cores=host_cores())
+    for name, err in zip(("dQ", "dK", "dV"), e):
+        assert err <= O_TOL, f"config {cfg}: {name} max abs error {err:.3e} > {O_TOL}"
+
+
+def _map_oracle(fn, jobs, threadpool_limits):
+    """fn over jobs on the host cores, one BLAS thread per worker."""
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(max(1, host_cores())) as ex:
+            return list(ex.map(fn, jobs))
+
+
 def test_one_million_tokens_document_tails():
     """2^20 packed tokens: dQ/dK/dV of the last rows of the longest and the
     last document (64-bit offsets past 2^31 bytes in dQ)."""

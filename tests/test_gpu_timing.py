@@ -40,7 +40,7 @@ def test_timer_counts_launches_and_matches_stream_events():
     api.timing_enable(False)
     # one schedule build for the forward, two for the backward (query-major and key-major)
     want = {api.KERNEL_SCHEDULE: 3, api.KERNEL_FWD: 1, api.KERNEL_DELTA: 0, api.KERNEL_DKDV: 1, api.KERNEL_DQ: 1,
-            api.KERNEL_MERGE: 1, api.KERNEL_CONVERT: 1, api.KERNEL_COPY: 0}
+            api.KERNEL_MERGE: 1, api.KERNEL_CONVERT: 1, api.KERNEL_COPY: 0, api.KERNEL_HEAD: 1}
     assert {k_: n for k_, (_, n) in c.items()} == want
     assert all((ms > 0) == (want[k_] > 0) for k_, (ms, _) in c.items())
 
