@@ -806,7 +806,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 // its chunks, keys in [kv_lo, kv_hi).  Disjoint outputs per workgroup: the
 // result does not depend on the order in which workgroups run.
 template <int D>
-__global__ __launch_bounds__(256) void head_kernel(BwdParams p, ChunkTable ch) {
+__global__ __launch_bounds__(256, 2) void head_kernel(BwdParams p, ChunkTable ch) {
   constexpr int H = kBwdHead;
   constexpr int DS = D + 4;             // LDS row stride (floats): 16-byte row reads of 16 rows on distinct banks
   constexpr int DG = D / 8;             // 8-wide d groups; 256 % DG == 0, so a thread keeps its d group
@@ -814,7 +814,7 @@ __global__ __launch_bounds__(256) void head_kernel(BwdParams p, ChunkTable ch) {
   constexpr int NKS = D / 16;
   static_assert(H == 32 || H == 64, "head block of one or three 32 x 32 MFMA tiles");
   constexpr int NTILE = H == 32 ? 1 : 3;
-  __shared__ __attribute__((aligned(16))) float ks[H][DS], qs[H][DS], dos[H][DS];
+  __shared__ __attribute__((aligned(16))) float ks[H][DS], vs[H][DS], qs[H][DS], dos[H][DS];
   __shared__ float ps[H][H + 1], dss[H][H + 1];
   __shared__ int rl[H];                 // local query row of head position t, -1 if not a row of this call
   __shared__ float lse2[H], dlt[H];
@@ -840,17 +840,20 @@ __global__ __launch_bounds__(256) void head_kernel(BwdParams p, ChunkTable ch) {
     }
     rl[tid] = loc;
   }
-  // K rows of the head keys (float, for dQ)
+  // K and V rows of the head keys (float: K for dQ, both for the S / dP
+  // operands, converted back to bf16 exactly)
   for (int t = tid; t < H * DG; t += 256) {
     const int c = t / DG;
-    float kf[8] = {};
+    float kf[8] = {}, vf[8] = {};
     if (c < nk) {
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(p.k + ((size_t)(k0 + c - p.kv_lo) * p.hkv + kvh) * D + dg0);
+      const size_t off = ((size_t)(k0 + c - p.kv_lo) * p.hkv + kvh) * D + dg0;
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(p.k + off);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(p.v + off);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = (float)kb[e];
+      for (int e = 0; e < 8; ++e) { kf[e] = (float)kb[e]; vf[e] = (float)vb[e]; }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ks[c][dg0 + e] = kf[e];
+    for (int e = 0; e < 8; ++e) { ks[c][dg0 + e] = kf[e]; vs[c][dg0 + e] = vf[e]; }
   }
   __syncthreads();
   bool any_row = false;
@@ -860,21 +863,9 @@ __global__ __launch_bounds__(256) void head_kernel(BwdParams p, ChunkTable ch) {
   // S and dP by v_mfma_f32_32x32x16_bf16 (exact bf16 products, fp32 sums):
   // wave 0 takes the 32 x 32 tile (rows 0-31, keys 0-31), and for H = 64
   // waves 1 and 2 the tiles (32-63, 0-31) and (32-63, 32-63); lane l holds
-  // key column l % 32 of its tile.  The K and V operands of this lane's key
-  // stay in registers for all heads.
+  // key column l % 32 of its tile; all operands come from the LDS rows.
   const int rt = wave == 0 ? 0 : 1, kt = wave == 2 ? 1 : 0;
   const int kcol = 32 * kt + l32;
-  bf16x8 kop[NKS], vop[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    kop[s] = bf16x8{};
-    vop[s] = bf16x8{};
-    if (wave < NTILE && kcol < nk) {
-      const size_t off = ((size_t)(k0 + kcol - p.kv_lo) * p.hkv + kvh) * D + 16 * s + 8 * hh;
-      kop[s] = *reinterpret_cast<const bf16x8*>(p.k + off);
-      vop[s] = *reinterpret_cast<const bf16x8*>(p.v + off);
-    }
-  }
 
   float dka[NT][8], dva[NT][8];         // dK, dV of keys (tid + 256 i) / DG, summed over the group's heads
 #pragma unroll
@@ -936,15 +927,21 @@ __global__ __launch_bounds__(256) void head_kernel(BwdParams p, ChunkTable ch) {
       const int row = 32 * rt + l32;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        bf16x8 qa = bf16x8{}, da = bf16x8{};
+        bf16x8 qa = bf16x8{}, da = bf16x8{}, kb = bf16x8{}, vb = bf16x8{};
         if (row < H) {
           const float* qr_ = &qs[row][16 * s + 8 * hh];
           const float* dr_ = &dos[row][16 * s + 8 * hh];
           qa = cvt8(qr_[0], qr_[1], qr_[2], qr_[3], qr_[4], qr_[5], qr_[6], qr_[7]);
           da = cvt8(dr_[0], dr_[1], dr_[2], dr_[3], dr_[4], dr_[5], dr_[6], dr_[7]);
         }
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vop[s], pacc, 0, 0, 0);
+        if (kcol < H) {
+          const float* kr_ = &ks[kcol][16 * s + 8 * hh];
+          const float* vr_ = &vs[kcol][16 * s + 8 * hh];
+          kb = cvt8(kr_[0], kr_[1], kr_[2], kr_[3], kr_[4], kr_[5], kr_[6], kr_[7]);
+          vb = cvt8(vr_[0], vr_[1], vr_[2], vr_[3], vr_[4], vr_[5], vr_[6], vr_[7]);
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, pacc, 0, 0, 0);
       }
     }
     if (wave < NTILE) {
