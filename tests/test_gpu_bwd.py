@@ -116,6 +116,34 @@ def test_split_kv_backward_sums_to_full():
     assert_close(dv.cpu().numpy(), wv, O_TOL, "split dV")
 
 
+def test_split_kv_backward_document_heads_across_block_cuts():
+    """KV blocks cut through the first 32 positions of documents, where the
+    backward computes pairs in float32 (the head pass): each block's call
+    takes only the pairs whose key is in its block, so the shares still sum
+    to the oracle's gradients, and to one call over the whole range."""
+    lengths = [10, 100, 40, 300, 150]                  # documents start at 0, 10, 110, 150, 450
+    cuts = [0, 20, 130, 160, 470, 600]                 # cut inside the heads of the last four
+    w = custom_workload(23, lengths, 8, 2, 128, backward=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    cu = w.cu_seqlens
+    o, lse = api.attn_fwd(qd, kd, vd, cu, w.chunks, 0, w.total, w.scale)
+    dq1, dk1, dv1 = api.attn_bwd(qd, kd, vd, o, lse, dod, cu, w.chunks, 0, w.total, w.scale)
+    dq = torch.zeros((w.tq, w.hq, w.d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.total, w.hkv, w.d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    for x, y in zip(cuts[:-1], cuts[1:]):
+        api.attn_bwd(qd, kd[x:y], vd[x:y], o, lse, dod, cu, w.chunks, x, y, w.scale, dq=dq, dk=dk[x:y],
+                     dv=dv[x:y], accumulate_dq=True)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.attention_backward(f64(q), f64(k), f64(v), f64(do), cu, w.chunks, 0, w.total, w.scale)
+    for name, got, single, want in (("dQ", dq, dq1, wq), ("dK", dk, dk1, wk), ("dV", dv, dv1, wv)):
+        assert_close(got.cpu().numpy(), want, O_TOL, f"split {name} vs oracle")
+        assert_close(single.cpu().numpy(), want, O_TOL, f"single {name} vs oracle")
+        # rows whose head is cut take Delta from the bf16 O instead of the head pass's own
+        assert_close(got.cpu().numpy(), single.cpu().numpy(), 5e-3, f"split vs single {name}")
+
+
 def test_split_kv_backward_ragged_last_block_delta_ready():
     """Split-KV backward whose second KV block is shorter than the first:
     Delta formed by the first call ([0, 8192)) and reused by the second
