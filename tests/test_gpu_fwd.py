@@ -123,6 +123,51 @@ def test_full_size_sampled_rows(cfg, seed):
                      config=cfg)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_full_size_every_document_head_every_head(cfg):
+    """Every document of the full-size workloads (canonical seeds), every
+    query head: its first <= 256 rows against the oracle over those rows and
+    keys (exact: a row attends only earlier keys of its document) -- the rows
+    with the fewest keys, whose probabilities are the largest."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    w = make_config(cfg)
+    print(f"[fwd] config {cfg} seed {w.seed}: every document's first rows", flush=True)
+    q, k, v = w.q(), w.k(), w.v()
+    o, lse = api.attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
+    o = bf16_to_np(o)
+    lse = lse.cpu().numpy()
+    cu = w.cu_seqlens
+    g = w.hq // w.hkv
+
+    def one(job):
+        doc, kvh = job
+        a, b = int(cu[doc]), int(cu[doc + 1])
+        n = min(b - a, 256)
+        heads = np.arange(kvh * g, (kvh + 1) * g)
+        wo, wl = oracle.attention_forward(f64(q[a:a + n][:, heads]), f64(k[a:a + n, kvh:kvh + 1]),
+                                          f64(v[a:a + n, kvh:kvh + 1]), cu, [(a, n)], a, a + n, w.scale)
+        return (float(np.abs(o[a:a + n][:, heads] - wo).max()), float(np.abs(lse[heads][:, a:a + n] - wl).max()))
+
+    jobs = [(doc, kvh) for doc in range(len(cu) - 1) for kvh in range(w.hkv)]
+
+    def run():
+        with threadpool_limits(limits=1):
+            with ThreadPoolExecutor(max(1, host_cores())) as ex:
+                return list(ex.map(one, jobs))
+
+    errs, secs = timed_s(run)
+    e = np.max(np.array(errs), axis=0)
+    print(f"[fwd] config {cfg}: {len(jobs)} (document, KV head) heads, max abs error O {e[0]:.2e} LSE {e[1]:.2e} "
+          f"(oracle {secs:.1f} s)", flush=True)
+    record(config=cfg, seed=w.seed, check="forward, every document's first rows on every head",
+           compared=f"first <= 256 rows of all {len(cu) - 1} documents, all {w.hq} heads",
+           err_O=e[0], err_LSE=e[1], oracle_s=round(secs, 2), cores=host_cores())
+    assert e[0] <= O_TOL, f"O max abs error {e[0]:.3e}"
+    assert e[1] <= LSE_TOL, f"LSE max abs error {e[1]:.3e}"
+
+
 @pytest.mark.parametrize("seed", [None, 11])
 def test_cp_rank_partials_and_merge(seed):
     """Rank 3 of CP = 8: per-chunk partials over the 8192-key blocks the need
