@@ -812,8 +812,7 @@ __global__ __launch_bounds__(256, 2) void head_kernel(BwdParams p, ChunkTable ch
   constexpr int DG = D / 8;             // 8-wide d groups; 256 % DG == 0, so a thread keeps its d group
   constexpr int NT = (H * DG + 255) / 256;   // (row or key, d group) tasks per thread
   constexpr int NKS = D / 16;
-  static_assert(H == 32 || H == 64, "head block of one or three 32 x 32 MFMA tiles");
-  constexpr int NTILE = H == 32 ? 1 : 3;
+  static_assert(H == 32, "the head block is one 32 x 32 MFMA tile");
   __shared__ __attribute__((aligned(16))) float ks[H][DS], vs[H][DS], qs[H][DS], dos[H][DS];
   __shared__ float ps[H][H + 1], dss[H][H + 1];
   __shared__ int rl[H];                 // local query row of head position t, -1 if not a row of this call
@@ -861,11 +860,9 @@ __global__ __launch_bounds__(256, 2) void head_kernel(BwdParams p, ChunkTable ch
   if (!any_row) return;                 // no head row among this call's query rows
 
   // S and dP by v_mfma_f32_32x32x16_bf16 (exact bf16 products, fp32 sums):
-  // wave 0 takes the 32 x 32 tile (rows 0-31, keys 0-31), and for H = 64
-  // waves 1 and 2 the tiles (32-63, 0-31) and (32-63, 32-63); lane l holds
-  // key column l % 32 of its tile; all operands come from the LDS rows.
-  const int rt = wave == 0 ? 0 : 1, kt = wave == 2 ? 1 : 0;
-  const int kcol = 32 * kt + l32;
+  // wave 0 takes the 32 x 32 tile, lane l holding key column l % 32; all
+  // operands come from the LDS rows.
+  const int kcol = l32;
 
   float dka[NT][8], dva[NT][8];         // dK, dV of keys (tid + 256 i) / DG, summed over the group's heads
 #pragma unroll
@@ -921,49 +918,36 @@ __global__ __launch_bounds__(256, 2) void head_kernel(BwdParams p, ChunkTable ch
     __syncthreads();
     if (hs + 1 < p.group) prefetch(head + 1);
     f32x16 sacc = f32x16{}, pacc = f32x16{};
-    if (wave < NTILE) {
+    if (wave == 0) {
       // A operands: this lane's row of the tile from the LDS rows (bf16
-      // values, so the conversion back is exact); rows past the head are zero
-      const int row = 32 * rt + l32;
+      // values, so the conversion back is exact)
+      const int row = l32;
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        bf16x8 qa = bf16x8{}, da = bf16x8{}, kb = bf16x8{}, vb = bf16x8{};
-        if (row < H) {
-          const float* qr_ = &qs[row][16 * s + 8 * hh];
-          const float* dr_ = &dos[row][16 * s + 8 * hh];
-          qa = cvt8(qr_[0], qr_[1], qr_[2], qr_[3], qr_[4], qr_[5], qr_[6], qr_[7]);
-          da = cvt8(dr_[0], dr_[1], dr_[2], dr_[3], dr_[4], dr_[5], dr_[6], dr_[7]);
-        }
-        if (kcol < H) {
-          const float* kr_ = &ks[kcol][16 * s + 8 * hh];
-          const float* vr_ = &vs[kcol][16 * s + 8 * hh];
-          kb = cvt8(kr_[0], kr_[1], kr_[2], kr_[3], kr_[4], kr_[5], kr_[6], kr_[7]);
-          vb = cvt8(vr_[0], vr_[1], vr_[2], vr_[3], vr_[4], vr_[5], vr_[6], vr_[7]);
-        }
+        const float* qr_ = &qs[row][16 * s + 8 * hh];
+        const float* dr_ = &dos[row][16 * s + 8 * hh];
+        const float* kr_ = &ks[kcol][16 * s + 8 * hh];
+        const float* vr_ = &vs[kcol][16 * s + 8 * hh];
+        const bf16x8 qa = cvt8(qr_[0], qr_[1], qr_[2], qr_[3], qr_[4], qr_[5], qr_[6], qr_[7]);
+        const bf16x8 da = cvt8(dr_[0], dr_[1], dr_[2], dr_[3], dr_[4], dr_[5], dr_[6], dr_[7]);
+        const bf16x8 kb = cvt8(kr_[0], kr_[1], kr_[2], kr_[3], kr_[4], kr_[5], kr_[6], kr_[7]);
+        const bf16x8 vb = cvt8(vr_[0], vr_[1], vr_[2], vr_[3], vr_[4], vr_[5], vr_[6], vr_[7]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, pacc, 0, 0, 0);
       }
     }
-    if (wave < NTILE) {
-      // element e of the tiles: row 32 rt + 8 (e / 4) + 4 hh + e % 4, key kcol;
+    if (wave == 0) {
+      // element e of the tile: row 8 (e / 4) + 4 hh + e % 4, key kcol;
       // pairs outside the head triangle (key after row), or of rows not in
       // this call, get P = 0
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int r = 32 * rt + 8 * (e >> 2) + 4 * hh + (e & 3);
-        if (r >= H || kcol >= H) continue;
+        const int r = 8 * (e >> 2) + 4 * hh + (e & 3);
         float pr = 0.f;
         if (r < nr && kcol < nk && kcol <= r && rl[r] >= 0)
           pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], p.scale_log2, -lse2[r]));
         ps[r][kcol] = pr;
         dss[r][kcol] = pacc[e];         // dP for now
-      }
-    } else if (NTILE == 3 && wave == 3) {
-      // wave 3: the tile (rows 0-31, keys 32-63) lies above the diagonal
-      for (int t = lane; t < 32 * (H - 32); t += 64) {
-        const int r = t / (H - 32), c = 32 + t % (H - 32);
-        ps[r][c] = 0.f;
-        dss[r][c] = 0.f;
       }
     }
     __syncthreads();
