@@ -7,10 +7,20 @@ import time
 import numpy as np
 import torch
 
-from document_masked_attention_amd.workloads import bf16_bits_to_f32
+from document_masked_attention_amd.workloads import bf16_bits_to_f32, custom_workload, lognormal_docs
 
 O_TOL = 2e-2      # max abs error on O, dQ, dK, dV (bf16 I/O)
 LSE_TOL = 1e-3    # max abs error on the LSE
+
+D64_LONG_LABEL = 6   # the parity table's row label of the workload below
+
+
+def d64_long_workload():
+    """Head size 64 at full size: 65536 tokens of lognormal(median 2048,
+    sigma 1.3) documents clipped to [64, 32768] (seed 65: 17 documents, the
+    longest 22,529 tokens), 16 query / 4 KV heads, forward and backward
+    inputs."""
+    return custom_workload(65, lognormal_docs(65, 2048, 1.3, 64, 32768, 65536), 16, 4, 64, backward=True)
 
 
 def to_dev(bits: np.ndarray) -> torch.Tensor:

@@ -13,7 +13,8 @@ NAMES = {1: "2048 tokens, docs [512,1024,256,256], 8/8 heads, d64 (fwd)",
          2: "32768 lognormal(1024,1.2), 32/8, d128 (fwd)",
          3: "CP rank 3 of 8, 131072 lognormal(2048,1.5), 32/8, d128 (fwd partials + merge)",
          4: "65536 lognormal(1024,1.2), 32/8, d128 (fwd+bwd)",
-         5: "131072 bimodal, 64/8, d128 (fwd+bwd)"}
+         5: "131072 bimodal, 64/8, d128 (fwd+bwd)",
+         6: "65536 lognormal(2048,1.3), 16/4, d64 (fwd+bwd; head size 64 at full size)"}
 
 
 def fmt(x, spec=".2e"):

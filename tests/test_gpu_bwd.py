@@ -16,7 +16,8 @@ import torch
 import oracle
 from document_masked_attention_amd import api
 from document_masked_attention_amd.workloads import custom_workload, make_config, random_lengths, Workload
-from gpu_util import to_dev, bf16_to_np, f64, assert_close, O_TOL, gpu_ms, timed_s, record, host_cores
+from gpu_util import (to_dev, f64, assert_close, O_TOL, gpu_ms, timed_s, record, host_cores,
+                      d64_long_workload, D64_LONG_LABEL)
 
 pytestmark = pytest.mark.gpu
 
@@ -218,57 +219,55 @@ def test_full_size_sampled_documents(cfg, seed):
            err_dQ=e[0], err_dK=e[1], err_dV=e[2], cores=host_cores())
 
 
+def _whole_document(w: Workload, q, k, v, do, grads, doc, kvh, label, what, ms=None):
+    """dQ, dK, dV of one whole document on one KV-head group against the
+    oracle sub-problem chunk = [a, b), KV = [a, b): exact, because a key is
+    attended only by rows of its own document."""
+    dq, dk, dv = grads
+    cu = w.cu_seqlens
+    g = w.hq // w.hkv
+    a, b = int(cu[doc]), int(cu[doc + 1])
+    heads = np.arange(kvh * g, (kvh + 1) * g)
+    tag = f"{label} doc {doc} [{a},{b}) ({b - a} tokens) kv head {kvh}"
+    print(f"[bwd] {tag}: oracle over the whole document", flush=True)
+    (wq, wk, wv), secs = timed_s(lambda: _oracle_backward_by_head(
+        f64(q[a:b][:, heads]), f64(k[a:b, kvh:kvh + 1]), f64(v[a:b, kvh:kvh + 1]), f64(do[a:b][:, heads]), cu,
+        [(a, b - a)], a, b, w.scale, tag))
+    eq = assert_close(dq[a:b][:, heads], wq, O_TOL, f"{tag} dQ")
+    ek = assert_close(dk[a:b, kvh:kvh + 1], wk, O_TOL, f"{tag} dK")
+    ev = assert_close(dv[a:b, kvh:kvh + 1], wv, O_TOL, f"{tag} dV")
+    print(f"[bwd] {tag}: max abs error dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e} (oracle {secs:.1f} s)", flush=True)
+    record(config=label, seed=w.seed, check=f"backward, whole document of {b - a} tokens ({what})",
+           compared=f"all {b - a} rows and keys, KV head {kvh} with its {g} query heads",
+           err_dQ=eq, err_dK=ek, err_dV=ev, gpu_ms=None if ms is None else round(ms, 3), oracle_s=round(secs, 2),
+           cores=host_cores())
+
+
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("cfg,ranks", [(4, (1,)), (5, (1, 2))])
 def test_full_size_whole_long_documents(cfg, ranks):
     """Whole long documents of the full-size workloads (canonical seeds): the
     longest (and, for the 131072-token mix, the second-longest) document,
-    every row and every key, one KV-head group.  A key is attended only by
-    rows of its own document, so the oracle sub-problem chunk = [a, b),
-    KV = [a, b) gives that document's exact dQ, dK and dV; this covers the
-    key-major work items' whole walks over the document's query blocks
-    (production guide, "Step 1: Establish a Single-GPU Numerical Baseline":
-    long sequences, not only short ones)."""
+    every row and every key, one KV-head group; this covers the key-major
+    work items' whole walks over the document's query blocks (production
+    guide, "Step 1: Establish a Single-GPU Numerical Baseline": long
+    sequences, not only short ones)."""
     w = make_config(cfg)
     print(f"[bwd] config {cfg} seed {w.seed}: generating inputs", flush=True)
     q, k, v, do = w.q(), w.k(), w.v(), w.do()
-    dq, dk, dv, ms = _gpu_fwd_bwd(w, q, k, v, do, with_ms=True)
-    cu = w.cu_seqlens
-    lengths = np.diff(cu)
-    order = np.argsort(-lengths, kind="stable")
-    g = w.hq // w.hkv
+    *grads, ms = _gpu_fwd_bwd(w, q, k, v, do, with_ms=True)
+    order = np.argsort(-np.diff(w.cu_seqlens), kind="stable")
     for rank in ranks:
-        doc = int(order[rank - 1])
-        a, b = int(cu[doc]), int(cu[doc + 1])
-        kvh = (3 * rank + cfg) % w.hkv
-        heads = np.arange(kvh * g, (kvh + 1) * g)
-        tag = f"config {cfg} doc {doc} [{a},{b}) ({b - a} tokens) kv head {kvh}"
-        print(f"[bwd] {tag}: oracle over the whole document", flush=True)
-        (wq, wk, wv), secs = timed_s(lambda: _oracle_backward_by_head(
-            f64(q[a:b][:, heads]), f64(k[a:b, kvh:kvh + 1]), f64(v[a:b, kvh:kvh + 1]), f64(do[a:b][:, heads]), cu,
-            [(a, b - a)], a, b, w.scale, tag))
-        eq = assert_close(dq[a:b][:, heads], wq, O_TOL, f"{tag} dQ")
-        ek = assert_close(dk[a:b, kvh:kvh + 1], wk, O_TOL, f"{tag} dK")
-        ev = assert_close(dv[a:b, kvh:kvh + 1], wv, O_TOL, f"{tag} dV")
-        print(f"[bwd] {tag}: max abs error dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e} (oracle {secs:.1f} s)", flush=True)
-        record(config=cfg, seed=w.seed, check=f"backward, whole document of {b - a} tokens (rank {rank} by length)",
-               compared=f"all {b - a} rows and keys, KV head {kvh} with its {g} query heads",
-               err_dQ=eq, err_dK=ek, err_dV=ev, gpu_ms=round(ms, 3), oracle_s=round(secs, 2), cores=host_cores())
+        _whole_document(w, q, k, v, do, grads, int(order[rank - 1]), (3 * rank + cfg) % w.hkv, cfg,
+                        f"rank {rank} by length", ms)
 
 
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_full_size_every_document_tail_every_kv_head(cfg):
-    """Every document of the full-size workloads (canonical seeds), every KV
-    head: its last <= 256 rows and keys against the oracle sub-problem (exact
-    there), so every short document is checked whole -- the rows with the
-    fewest keys, whose P and dS are the largest, are where rounding them to
-    the bf16 matrix-core operands costs the most."""
+def _every_document_tail(w: Workload, q, k, v, do, grads, label):
+    """Every document, every KV head: its last <= 256 rows and keys against
+    the oracle sub-problem (exact there), so every short document is checked
+    whole."""
     from threadpoolctl import threadpool_limits
-    w = make_config(cfg)
-    print(f"[bwd] config {cfg} seed {w.seed}: generating inputs", flush=True)
-    q, k, v, do = w.q(), w.k(), w.v(), w.do()
-    dq, dk, dv = _gpu_fwd_bwd(w, q, k, v, do)
+    dq, dk, dv = grads
     cu = w.cu_seqlens
     g = w.hq // w.hkv
     jobs = [(doc, kvh) for doc in range(len(cu) - 1) for kvh in range(w.hkv)]
@@ -286,13 +285,40 @@ def test_full_size_every_document_tail_every_kv_head(cfg):
 
     errs, secs = timed_s(lambda: _map_oracle(one, jobs, threadpool_limits))
     e = np.max(np.array(errs), axis=0)
-    print(f"[bwd] config {cfg}: {len(jobs)} (document, KV head) tails, max abs error dQ {e[0]:.2e} dK {e[1]:.2e} "
+    print(f"[bwd] {label}: {len(jobs)} (document, KV head) tails, max abs error dQ {e[0]:.2e} dK {e[1]:.2e} "
           f"dV {e[2]:.2e} (oracle {secs:.1f} s)", flush=True)
-    record(config=cfg, seed=w.seed, check="backward, every document tail on every KV head",
+    record(config=label, seed=w.seed, check="backward, every document tail on every KV head",
            compared=f"last <= 256 rows and keys of all {len(cu) - 1} documents x {w.hkv} KV-head groups",
            err_dQ=e[0], err_dK=e[1], err_dV=e[2], oracle_s=round(secs, 2), cores=host_cores())
     for name, err in zip(("dQ", "dK", "dV"), e):
-        assert err <= O_TOL, f"config {cfg}: {name} max abs error {err:.3e} > {O_TOL}"
+        assert err <= O_TOL, f"{label}: {name} max abs error {err:.3e} > {O_TOL}"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_full_size_every_document_tail_every_kv_head(cfg):
+    """Every document of the full-size workloads (canonical seeds) on every KV
+    head -- the rows with the fewest keys, whose P and dS are the largest, are
+    where rounding them to the bf16 matrix-core operands costs the most."""
+    w = make_config(cfg)
+    print(f"[bwd] config {cfg} seed {w.seed}: generating inputs", flush=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    _every_document_tail(w, q, k, v, do, _gpu_fwd_bwd(w, q, k, v, do), cfg)
+
+
+@pytest.mark.timeout(900)
+def test_d64_long_documents():
+    """Head size 64 at full size (the D = 64 kernels have their own LDS
+    layouts and tile walks): the 65536-token lognormal mix whose longest
+    document has 22,529 tokens, 16 query / 4 KV heads.  That document whole on
+    one KV-head group, and every document's tail on every KV head."""
+    w = d64_long_workload()
+    print(f"[bwd] d64 long documents seed {w.seed}: generating inputs", flush=True)
+    q, k, v, do = w.q(), w.k(), w.v(), w.do()
+    *grads, ms = _gpu_fwd_bwd(w, q, k, v, do, with_ms=True)
+    longest = int(np.argmax(np.diff(w.cu_seqlens)))
+    _whole_document(w, q, k, v, do, grads, longest, 1, D64_LONG_LABEL, "the longest", ms)
+    _every_document_tail(w, q, k, v, do, grads, D64_LONG_LABEL)
 
 
 def _map_oracle(fn, jobs, threadpool_limits):

@@ -12,10 +12,9 @@ import torch
 
 import oracle
 from document_masked_attention_amd import api
-from document_masked_attention_amd.workloads import (custom_workload, make_config, random_lengths,
-                                                     cu_from_lengths, Workload)
+from document_masked_attention_amd.workloads import custom_workload, make_config, random_lengths, Workload
 from gpu_util import (to_dev, bf16_to_np, f64, assert_close, O_TOL, LSE_TOL, gpu_ms, timed_s, record,
-                      host_cores)
+                      host_cores, d64_long_workload, D64_LONG_LABEL)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,18 +122,12 @@ def test_full_size_sampled_rows(cfg, seed):
                      config=cfg)
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_full_size_every_document_head_every_head(cfg):
-    """Every document of the full-size workloads (canonical seeds), every
-    query head: its first <= 256 rows against the oracle over those rows and
-    keys (exact: a row attends only earlier keys of its document) -- the rows
-    with the fewest keys, whose probabilities are the largest."""
+def _every_document_head(w: Workload, q, k, v, label):
+    """GPU forward of the whole workload; every document's first <= 256 rows on
+    every query head against the oracle over those rows and keys (exact: a row
+    attends only earlier keys of its document).  Returns the largest errors."""
     from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
-    w = make_config(cfg)
-    print(f"[fwd] config {cfg} seed {w.seed}: every document's first rows", flush=True)
-    q, k, v = w.q(), w.k(), w.v()
     o, lse = api.attn_fwd(to_dev(q), to_dev(k), to_dev(v), w.cu_seqlens, w.chunks, w.kv_lo, w.kv_hi, w.scale)
     o = bf16_to_np(o)
     lse = lse.cpu().numpy()
@@ -159,13 +152,37 @@ def test_full_size_every_document_head_every_head(cfg):
 
     errs, secs = timed_s(run)
     e = np.max(np.array(errs), axis=0)
-    print(f"[fwd] config {cfg}: {len(jobs)} (document, KV head) heads, max abs error O {e[0]:.2e} LSE {e[1]:.2e} "
+    print(f"[fwd] {label}: {len(jobs)} (document, KV head) heads, max abs error O {e[0]:.2e} LSE {e[1]:.2e} "
           f"(oracle {secs:.1f} s)", flush=True)
-    record(config=cfg, seed=w.seed, check="forward, every document's first rows on every head",
+    record(config=label, seed=w.seed, check="forward, every document's first rows on every head",
            compared=f"first <= 256 rows of all {len(cu) - 1} documents, all {w.hq} heads",
            err_O=e[0], err_LSE=e[1], oracle_s=round(secs, 2), cores=host_cores())
     assert e[0] <= O_TOL, f"O max abs error {e[0]:.3e}"
     assert e[1] <= LSE_TOL, f"LSE max abs error {e[1]:.3e}"
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_full_size_every_document_head_every_head(cfg):
+    """Every document of the full-size workloads (canonical seeds), every
+    query head: its first <= 256 rows against the oracle over those rows and
+    keys -- the rows with the fewest keys, whose probabilities are the largest."""
+    w = make_config(cfg)
+    print(f"[fwd] config {cfg} seed {w.seed}: every document's first rows", flush=True)
+    _every_document_head(w, w.q(), w.k(), w.v(), cfg)
+
+
+@pytest.mark.timeout(600)
+def test_d64_long_documents():
+    """Head size 64 at full size (the D = 64 kernels have their own LDS
+    layouts and tile walks): the 65536-token lognormal mix with a
+    22,529-token document, 16 query / 4 KV heads.  Sampled rows (first and
+    last rows of documents among them) against the oracle over the whole
+    key range, then every document's first <= 256 rows on every head."""
+    w = d64_long_workload()
+    _run_and_compare(w, rows=_sample_rows(w, 128, D64_LONG_LABEL), tag="d64 long documents sampled",
+                     config=D64_LONG_LABEL)
+    _every_document_head(w, w.q(), w.k(), w.v(), D64_LONG_LABEL)
 
 
 @pytest.mark.parametrize("seed", [None, 11])
