@@ -41,7 +41,7 @@ def _run_and_compare(w: Workload, rows=None, tag="", config=None):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (12, 2), (8, 1), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (12, 2), (8, 1), (16, 2), (32, 2)])
 def test_small_random(d, hq, hkv):
     rng = np.random.default_rng(1000 + d + 10 * hq + hkv)
     total = int(rng.integers(300, 700))
