@@ -13,19 +13,25 @@
 // only on PARTIAL tiles.  K and V tiles (64 keys) are staged in LDS and shared
 // by the 4 waves (GQA heads and/or row blocks).
 //
-// MFMA formulation (v_mfma_f32_32x32x16_bf16, wave64):
-//   S^T[key][q] = K Q^T   (A = K rows from LDS, B = Q held in registers)
+// MFMA formulation (v_mfma_f32_16x16x32_bf16, wave64; a wave's 32 rows are
+// two 16-row halves):
+//   S^T[key][q] = K Q^T   (A = 16 K rows from LDS, B = Q held in registers;
+//                          every K operand feeds both halves)
 //   O^T[d][q]  += V^T P^T (A = V^T from LDS, B = P^T straight from the S^T
 //                          accumulators, converted to bf16)
-// With keys on the accumulator rows, a query's scores sit in one lane pair
-// (lane and lane^32), so row max/sum are in-register plus one cross-half swap.
-// The accumulator row order of S^T is {0-3, 8-11 | 4-7, 12-15} per 16 keys for
-// the two lane halves; the V^T operand is gathered in that same key order from
-// the row-major V tile with LDS transpose reads (ds_read_b64_tr_b16).
+// Lane l holds query row l mod 16 of each half and, per 16 keys, the four
+// keys 4 (l / 16) .. +3; a row's scores sit in four lanes (l mod 16 equal),
+// joined only for the tile maximum and the final sum.  P^T of 32 keys is the B
+// operand in the key order {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3} for lane
+// group g; the V^T operand is gathered in that same order from the row-major V
+// tile with LDS transpose reads (ds_read_b64_tr_b16).  Against the 32 x 32 x 16
+// instruction this moves half the accumulator data per product, which measured
+// ~2% faster here at the same LDS traffic (the matrix cores take less power per
+// product).
 // K/V tiles are double-buffered in LDS (filled by direct global-to-LDS loads)
 // with one barrier per tile; after a tile's softmax the MFMAs of the next
-// tile's S^T and of this tile's PV run back to back, while the other wave on
-// the SIMD works on its softmax.
+// tile's S^T and of this tile's PV run back to back as one stream of
+// prefetched operands, while the other wave on the SIMD works on its softmax.
 #include "kernels.h"
 
 #include <type_traits>
@@ -46,15 +52,15 @@ template <int D, int RB, int HB>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   static_assert(RB * HB == 4, "four waves per workgroup");
   constexpr int BK = kFwdBK;
-  constexpr int KSTR = D + 8;           // K row stride (bf16): 16-byte row reads hit distinct banks
-  constexpr int VSTR = D + 32;          // V row stride: transpose reads of 4 rows hit distinct banks
+  constexpr int KSTR = D + 8;           // K row stride (bf16): 16-byte row reads of 16 rows hit distinct banks
+  constexpr int VSTR = D + 16;          // V row stride: transpose reads of 8 rows x 4 columns hit distinct banks
   constexpr int CPK = D / 8;            // 16-byte chunks per key row
   constexpr int KCH = KSTR / 8, VCH = VSTR / 8;       // 16-byte slots per LDS row (data + padding)
   constexpr int WLK = BK * KCH / 64, WLV = BK * VCH / 64;   // direct loads (64 slots) per tile
   static_assert(BK * KCH % 64 == 0 && BK * VCH % 64 == 0, "tiles are whole direct loads");
   constexpr int DPK = (WLK + 3) / 4, DPV = (WLV + 3) / 4;   // per wave (the last may be idle)
-  constexpr int NKS = D / 16;           // k-steps of QK^T
-  constexpr int NDB = D / 32;           // 32-wide d blocks of O
+  constexpr int NKS = D / 32;           // 32-wide k-steps of QK^T
+  constexpr int NDB = D / 16;           // 16-wide d blocks of O
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BK * VSTR];
 
@@ -67,34 +73,43 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int l_row0 = pl[QP_LROW0], g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
   const int kt_lo = pl[QP_KT_LO], kt_flo = pl[QP_KT_FLO], kt_fhi = pl[QP_KT_FHI], kt_hi = pl[QP_KT_HI];
 
+  // Lane l works on rows 16 r + (l mod 16) of the wave's 32 (r = 0, 1: the two
+  // 16-row halves) and, in every 16 x 16 accumulator, on the four rows of
+  // group g = l / 16.
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
+  const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, i16 = lane & 15;
   const int rb = wave / HB, hs = wave % HB;
   const int head = kvh * p.group + hb * HB + hs;
-  const int qr = 32 * rb + ln;
-  const bool row_ok = qr < nrows;
-  const int gi = g_row0 + qr;
-  const size_t o_off = ((size_t)(l_row0 + qr) * p.hq + head) * D;
-  // allowed keys of this row: [a_lo, a_lo + a_w] (global positions); empty rows never match
-  int a_lo = 0x40000000, a_w = 0;
-  if (row_ok) {
-    const int lo = max(doc_start(p.cu, p.n_docs, gi), p.kv_lo), hi = min(gi, p.kv_hi - 1);
-    if (hi >= lo) { a_lo = lo; a_w = hi - lo; }
+  int qr[2], a_lo[2], a_w[2];
+  bool row_ok[2];
+  size_t o_off[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    qr[r] = 32 * rb + 16 * r + i16;
+    row_ok[r] = qr[r] < nrows;
+    o_off[r] = ((size_t)(l_row0 + qr[r]) * p.hq + head) * D;
+    // allowed keys of this row: [a_lo, a_lo + a_w] (global positions); empty rows never match
+    a_lo[r] = 0x40000000;
+    a_w[r] = 0;
+    if (row_ok[r]) {
+      const int gi = g_row0 + qr[r];
+      const int lo = max(doc_start(p.cu, p.n_docs, gi), p.kv_lo), hi = min(gi, p.kv_hi - 1);
+      if (hi >= lo) { a_lo[r] = lo; a_w[r] = hi - lo; }
+    }
   }
 
-  bf16x8 qf[NKS];            // Q operand of this lane: row qr, d = 16 s + 8 hh .. +8, k-step s
+  bf16x8 qf[2][NKS];         // Q operand: row 16 r + l mod 16, d = 32 s + 8 g .. +8, k-step s
 
-  f32x16 oacc[NDB];
+  f32x4 oacc[NDB][2];        // O^T: d = 16 b + 4 g + e, row 16 r + l mod 16
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) oacc[b] = f32x16{};
-  float m_run = -INFINITY;   // softmax reference (scale*log2(e) units)
-  float l_run = 0.f;         // this lane half's share of the exp-sum
+  for (int b = 0; b < NDB; ++b) oacc[b][0] = oacc[b][1] = f32x4{};
+  float m_run[2] = {-INFINITY, -INFINITY};   // softmax reference per row (scale*log2(e) units)
+  float l_run[2] = {0.f, 0.f};               // this lane's share of the row's exp-sum
 
   const int tkv = p.kv_hi - p.kv_lo;
   const size_t kv_rstride = (size_t)p.hkv * D;
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
-
   // K and V tiles reach LDS by direct global-to-LDS loads (no staging
   // registers; completion by this wave's vmcnt, then a barrier).  A tile of
   // padded rows is a run of 16-byte slots; direct load j (of a wave: j = wave
@@ -151,25 +166,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   auto issue_v = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
     issue_rows(vbase, kt, lds, vrow, vchk, std::integral_constant<int, DPV>{}, std::integral_constant<int, WLV>{});
   };
-  // transpose-read source address of this lane inside a V tile (see lds_read_tr16)
-  const int i16 = lane & 15;
-  const int vt_off = (4 * hh + (i16 >> 2)) * VSTR + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  // Transpose-read source address of this lane inside a V tile (see
+  // lds_read_tr16): as the supplier of group g, lane l names row 4 g + (l mod
+  // 16) / 4 and column 4 (l mod 4) of a 16-key x 16-column block, so that
+  // lane l of the group receives rows 4 g .. 4 g + 3 of column l mod 16.
+  const int vt_off = (4 * g4 + (i16 >> 2)) * VSTR + 4 * (i16 & 3);
 
-  // S^T = K Q^T for the two 32-key blocks of the tile held in K buffer kb_
-  auto compute_s = [&](const uint16_t* kl, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
-    constexpr int NT = 2 * NKS, PFS = 4;
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
+  // S^T = K Q^T over the tile held in K buffer kl: 4 blocks of 16 keys x the
+  // two 16-row halves, D / 32 k-steps; every K operand feeds both halves
+  auto compute_s = [&](const uint16_t* kl, f32x4 (&sacc)[4][2]) __attribute__((always_inline)) {
+    constexpr int NT = 4 * NKS, PFS = 4;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sacc[kb][0] = sacc[kb][1] = f32x4{};
     bf16x8 op[NT];
     auto load = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      op[i] = *reinterpret_cast<const bf16x8*>(&kl[(32 * (i % 2) + ln) * KSTR + 16 * (i / 2) + 8 * hh]);
+      op[i] = *reinterpret_cast<const bf16x8*>(&kl[(16 * (i % 4) + i16) * KSTR + 32 * (i / 4) + 8 * g4]);
     };
     static_for<PFS>([&](auto ic) __attribute__((always_inline)) { load(ic); });
     static_for<NT>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + PFS < NT) load(std::integral_constant<int, i + PFS>{});
-      sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[i / 2], sacc[i % 2], 0, 0, 0);
+      sacc[i % 4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[i], qf[0][i / 4], sacc[i % 4][0], 0, 0, 0);
+      sacc[i % 4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[i], qf[1][i / 4], sacc[i % 4][1], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -178,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // k_lds[u & 1] and V tile u in v_lds[u & 1].  Step u computes S(u + 1) right
   // after the softmax of tile u, so K is staged two tiles ahead and V one.
   const int n = kt_hi - kt_lo;
-  f32x16 s_cur[2];
+  f32x4 s_cur[4][2];
   if (n > 0) {
     issue_k(kt_lo, k_lds[0]);
     issue_v(kt_lo, v_lds[0]);
@@ -186,10 +205,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   }
   // the first tiles are in flight while the Q operands load
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    if (row_ok) qf[s] = *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh);
-    else qf[s] = bf16x8{};
-  }
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      if (row_ok[r]) qf[r][s] = *reinterpret_cast<const bf16x8*>(p.q + o_off[r] + 32 * s + 8 * g4);
+      else qf[r][s] = bf16x8{};
+    }
   if (n > 0) {
     wait_vmem();
     __syncthreads();
@@ -199,7 +220,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // the Q operands are in registers before any tile loads are in flight (a
   // first use inside the loop would wait for all of them)
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) asm volatile("" ::"v"(qf[s]));
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) asm volatile("" ::"v"(qf[r][s]));
   // One pipeline step; `has_next` is a compile-time flag so that the steady-state
   // body has no branches between the next tile's MFMAs and this tile's softmax.
   auto step = [&](int u, auto has_next_c) __attribute__((always_inline)) {
@@ -215,73 +238,116 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // document mask on PARTIAL tiles and on the ragged last tile (its padding
     // keys lie beyond kv_hi even when every real pair is allowed)
     if (kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv) {
-      const int rel0 = p.kv_lo + kt * BK + 4 * hh - a_lo;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 2; ++r) {
+        const int rel0 = p.kv_lo + kt * BK + 4 * g4 - a_lo[r];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const unsigned rel = (unsigned)(rel0 + 32 * kb + 8 * (r >> 2) + (r & 3));
-          if (rel > (unsigned)a_w) s_cur[kb][r] = -INFINITY;
-        }
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned rel = (unsigned)(rel0 + 16 * kb + e);
+            if (rel > (unsigned)a_w[r]) s_cur[kb][r][e] = -INFINITY;
+          }
+      }
     }
-    // online softmax (base 2) against the running reference (see kAcceptSum)
-    float rs = 0.f;
-    bf16x8 pf[4];
-    auto exps = [&](float m_use) __attribute__((always_inline)) {
-      float r_ = 0.f;
+    // online softmax (base 2) against the running reference (see kAcceptSum).
+    // P^T of key block pair (2 t, 2 t + 1) is the B operand of k-step t of
+    // PV, in the key order {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3}.
+    float rs[2] = {0.f, 0.f};
+    bf16x8 pf[2][2];
+    auto exps = [&](const float (&m_use)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 2; ++r) {
+        float r_ = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], p.scale_log2, -m_use));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r + 1], p.scale_log2, -m_use));
-          r_ += e0 + e1;
-          const bf16x2 two = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
-          pf[2 * kb + (r >> 3)][r & 7] = two[0];
-          pf[2 * kb + (r >> 3)][(r & 7) + 1] = two[1];
-        }
-      return r_;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r][e], p.scale_log2, -m_use[r]));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r][e + 1], p.scale_log2, -m_use[r]));
+            r_ += e0 + e1;
+            const bf16x2 two = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
+            pf[kb >> 1][r][4 * (kb & 1) + e] = two[0];
+            pf[kb >> 1][r][4 * (kb & 1) + e + 1] = two[1];
+          }
+        rs[r] = r_;
+      }
     };
     bool redo = true;
-    if (!__any(m_run == -INFINITY)) {
-      rs = exps(m_run);
-      redo = __any(rs > kAcceptSum);
+    if (!__any(m_run[0] == -INFINITY || m_run[1] == -INFINITY)) {
+      exps(m_run);
+      redo = __any(rs[0] > kAcceptSum || rs[1] > kAcceptSum);
     }
     if (redo) {
-      float mx = -INFINITY;
+      float m_new[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 2; ++r) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
-      const float m_new = fmaxf(m_run, pair_max32(mx) * p.scale_log2);
-      if (__any(m_new > m_run)) {
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s_cur[kb][r][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));        // the row's four lanes (g = 0 .. 3)
+        m_new[r] = fmaxf(m_run[r], pair_max32(mx) * p.scale_log2);
       }
-      rs = exps(m_run == -INFINITY ? 0.f : m_run);
+      if (__any(m_new[0] > m_run[0] || m_new[1] > m_run[1])) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const float alpha = m_new[r] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[r] - m_new[r]);
+          m_run[r] = m_new[r];
+          l_run[r] *= alpha;
+#pragma unroll
+          for (int b = 0; b < NDB; ++b) oacc[b][r] *= alpha;
+        }
+      }
+      const float m_use[2] = {m_run[0] == -INFINITY ? 0.f : m_run[0], m_run[1] == -INFINITY ? 0.f : m_run[1]};
+      exps(m_use);
     }
-    l_run += rs;
-    // S of the next tile, into the registers this tile's softmax has just
-    // read; those MFMAs and this tile's PV run back to back, at raised wave
-    // priority so that the matrix core is fed first while the other wave of
-    // the SIMD runs its softmax
+    l_run[0] += rs[0];
+    l_run[1] += rs[1];
+    // One stream of MFMA operands, each feeding both row halves: the K
+    // fragments of the next tile's S (into the registers this tile's softmax
+    // has just read), then the V^T fragments of this tile's PV (32 keys per
+    // k-step, from the row-major V tile through transpose reads in P^T's key
+    // order).  Every fragment is read PF slots ahead, across the S / PV
+    // boundary too.  The block runs at raised wave priority so that the
+    // matrix core is fed first while the other wave of the SIMD runs its
+    // softmax.
     __builtin_amdgcn_s_setprio(1);
-    if (has_next) compute_s(k_lds[(u + 1) & 1], s_cur);
-
-    // O^T += V^T P^T, 16 keys per step; V^T comes from the row-major V tile
-    // through transpose reads, in the accumulator's permuted key order
-    const uint16_t* vl = v_lds[u & 1];
+    {
+      constexpr int NS = has_next ? 4 * NKS : 0, NSLOT = NS + 2 * NDB, PF = 4;
+      const uint16_t* kl = k_lds[(u + 1) & 1];
+      const uint16_t* vl = v_lds[u & 1];
+      if (has_next) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int b = 0; b < NDB; ++b) {
-        const uint16_t* vp = vl + vt_off + 16 * s * VSTR + 32 * b;
-        const bf16x8 vf = tr_operand(vp, vp + 8 * VSTR);
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[b], 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb) s_cur[kb][0] = s_cur[kb][1] = f32x4{};
       }
+      bf16x8 opr[NSLOT];
+      auto load = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < NS) {
+          opr[i] = *reinterpret_cast<const bf16x8*>(&kl[(16 * (i % 4) + i16) * KSTR + 32 * (i / 4) + 8 * g4]);
+        } else {
+          constexpr int t = (i - NS) / NDB, b = (i - NS) % NDB;
+          const uint16_t* vp = vl + vt_off + 32 * t * VSTR + 16 * b;
+          opr[i] = tr_operand(vp, vp + 16 * VSTR);
+        }
+      };
+      static_for<PF>([&](auto ic) __attribute__((always_inline)) { load(ic); });
+      static_for<NSLOT>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + PF < NSLOT) load(std::integral_constant<int, i + PF>{});
+        if constexpr (i < NS) {
+          s_cur[i % 4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opr[i], qf[0][i / 4], s_cur[i % 4][0], 0, 0, 0);
+          s_cur[i % 4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opr[i], qf[1][i / 4], s_cur[i % 4][1], 0, 0, 0);
+        } else {
+          constexpr int t = (i - NS) / NDB, b = (i - NS) % NDB;
+          oacc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opr[i], pf[t][0], oacc[b][0], 0, 0, 0);
+          oacc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opr[i], pf[t][1], oacc[b][1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
     __builtin_amdgcn_s_setprio(0);
     if (has_next) {
       wait_vmem();
@@ -292,33 +358,31 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (n > 0) step(n - 1, std::false_type{});
 
   // epilogue: normalise, write O (bf16, or float32 partials) and LSE (natural log)
-  const float l_tot = pair_sum32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row_ok && p.o32) {
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
+  for (int r = 0; r < 2; ++r) {
+    const float l_half = l_run[r] + __shfl_xor(l_run[r], 16);
+    const float l_tot = pair_sum32(l_half);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row_ok[r] && p.o32) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 val = make_float4(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv, oacc[b][4 * g + 2] * inv,
-                                       oacc[b][4 * g + 3] * inv);
-        *reinterpret_cast<float4*>(p.o32 + o_off + 32 * b + 8 * g + 4 * hh) = val;
+      for (int b = 0; b < NDB; ++b) {
+        const float4 val = make_float4(oacc[b][r][0] * inv, oacc[b][r][1] * inv, oacc[b][r][2] * inv,
+                                       oacc[b][r][3] * inv);
+        *reinterpret_cast<float4*>(p.o32 + o_off[r] + 16 * b + 4 * g4) = val;
       }
-  } else if (row_ok) {
+    } else if (row_ok[r]) {
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const bf16x2 lo2 = __builtin_convertvector(f32x2{oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv}, bf16x2);
-        const bf16x2 hi2 = __builtin_convertvector(f32x2{oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv}, bf16x2);
+      for (int b = 0; b < NDB; ++b) {
+        const bf16x2 lo2 = __builtin_convertvector(f32x2{oacc[b][r][0] * inv, oacc[b][r][1] * inv}, bf16x2);
+        const bf16x2 hi2 = __builtin_convertvector(f32x2{oacc[b][r][2] * inv, oacc[b][r][3] * inv}, bf16x2);
         uint2 val;
         val.x = *reinterpret_cast<const uint32_t*>(&lo2);
         val.y = *reinterpret_cast<const uint32_t*>(&hi2);
-        *reinterpret_cast<uint2*>(p.o + o_off + 32 * b + 8 * g + 4 * hh) = val;
+        *reinterpret_cast<uint2*>(p.o + o_off[r] + 16 * b + 4 * g4) = val;
       }
-  }
-  if (row_ok) {
-    if (hh == 0)
-      p.lse[(size_t)head * p.tq + l_row0 + qr] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    if (row_ok[r] && g4 == 0)
+      p.lse[(size_t)head * p.tq + l_row0 + qr[r]] = l_tot > 0.f ? (m_run[r] + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
