@@ -14,12 +14,14 @@
 //
 // * dq_kernel, query-major, shaped like the forward.  Work item = (query tile,
 //   KV head, block of query heads), 4 waves, two workgroups per CU; each
-//   wave owns 32 rows x 1 head.
+//   wave owns 32 rows x 1 head (two 16-row halves).
 //   It first forms Delta of its rows (unless the caller supplied it) from the
 //   dO operands it holds and the O rows, and stores it; then it walks the
-//   tile's KV range:
+//   tile's KV range, 32 keys at a time:
 //     S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T
-//   (v_mfma_f32_32x32x16_bf16; K^T through transpose reads).
+//   (v_mfma_f32_16x16x32_bf16, every K, V and K^T operand feeding both row
+//   halves; K^T through transpose reads; dS^T straight from the
+//   accumulators, in the forward's permuted key order).
 // * dkdv_kernel, key-major.  Work item = (one or two KV tiles of 128 keys
 //   of a document, paired by the scheduler, KV head); 4 waves x 32 keys (one
 //   wave per SIMD), each lane keeping one key's K and V rows (MFMA B
@@ -572,8 +574,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   using L = SwzTile<D>;                 // K tile: row chunks and transpose reads
   constexpr int VS = D + 8;             // V tile: row chunks only (padded rows)
   constexpr int CPK = D / 8;
-  constexpr int NKS = D / 16;
-  constexpr int NDB = D / 32;
+  constexpr int NKS = D / 32;           // 32-wide k-steps of S^T and dP^T
+  constexpr int NDB = D / 16;           // 16-wide d blocks of dQ
   // K and V tiles reach LDS by direct global-to-LDS loads: a tile is a run of
   // 16-byte slots (SK / SV per row: the row's chunks plus padding slots), and
   // direct load j fills slots 64 j .. 64 j + 63.  Lane l of load j maps slot
@@ -597,14 +599,23 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int l_row0 = pl[QP_LROW0], g_row0 = pl[QP_GROW0], nrows = pl[QP_NROWS];
   const int kt_lo = pl[QP_KT_LO], kt_flo = pl[QP_KT_FLO], kt_fhi = pl[QP_KT_FHI], kt_hi = pl[QP_KT_HI];
 
+  // Lane l works on rows 16 r + (l mod 16) of the wave's 32 (r = 0, 1: the two
+  // 16-row halves) and, in every 16 x 16 accumulator, on the four rows of
+  // group g = l / 16.
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, ln = lane & 31;
+  const int wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, i16 = lane & 15;
   const int rb = wave / HB, hs = wave % HB;
   const int head = kvh * p.group + hb * HB + hs;
-  const int qr = 32 * rb + ln;
-  const bool row_ok = qr < nrows;
-  const int gi = g_row0 + qr;
-  const size_t o_off = ((size_t)(l_row0 + qr) * p.hq + head) * D;
+  int qr[2], gi[2];
+  bool row_ok[2];
+  size_t o_off[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    qr[r] = 32 * rb + 16 * r + i16;
+    row_ok[r] = qr[r] < nrows;
+    gi[r] = g_row0 + qr[r];
+    o_off[r] = ((size_t)(l_row0 + qr[r]) * p.hq + head) * D;
+  }
   const int tkv = p.kv_hi - p.kv_lo;
   const size_t kv_rstride = (size_t)p.hkv * D;
   const uint16_t* kbase = p.k + (size_t)kvh * D;
@@ -649,69 +660,81 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   // the first K / V tile is in flight while the row operands load
   const int n = kt_hi - kt_lo;
   if (n > 0) issue_tile(kt_lo, std::integral_constant<int, 0>{});
-  int a_lo = 0x40000000, a_w = 0;
-  float lse2 = INFINITY, dlt = 0.f;
-  if (row_ok) {
-    // a row among its document's first kBwdHead positions attends only keys
-    // among them: all of its pairs belong to the head pass (fp32)
-    const int ds = doc_start(p.cu, p.n_docs, gi);
-    const int lo = max(ds, p.kv_lo), hi = min(gi, p.kv_hi - 1);
-    if (hi >= lo && gi - ds >= kBwdHead) { a_lo = lo; a_w = hi - lo; }
-    const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr];
-    lse2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
-    if (p.delta_ready) dlt = p.delta[(size_t)head * p.tq + l_row0 + qr];
-  }
-  bf16x8 qf[NKS], dof[NKS];
+  int a_lo[2], a_w[2];
+  float lse2[2], dlt[2];
+  bf16x8 qf[2][NKS], dof[2][NKS];      // row 16 r + l mod 16, d = 32 s + 8 g .. +8, k-step s
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    qf[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.q + o_off + 16 * s + 8 * hh) : bf16x8{};
-    dof[s] = row_ok ? *reinterpret_cast<const bf16x8*>(p.d_o + o_off + 16 * s + 8 * hh) : bf16x8{};
+  for (int r = 0; r < 2; ++r) {
+    a_lo[r] = 0x40000000;
+    a_w[r] = 0;
+    lse2[r] = INFINITY;
+    dlt[r] = 0.f;
+    if (row_ok[r]) {
+      // a row among its document's first kBwdHead positions attends only keys
+      // among them: all of its pairs belong to the head pass (fp32)
+      const int ds = doc_start(p.cu, p.n_docs, gi[r]);
+      const int lo = max(ds, p.kv_lo), hi = min(gi[r], p.kv_hi - 1);
+      if (hi >= lo && gi[r] - ds >= kBwdHead) { a_lo[r] = lo; a_w[r] = hi - lo; }
+      const float lv = p.lse[(size_t)head * p.tq + l_row0 + qr[r]];
+      lse2[r] = lv == -INFINITY ? INFINITY : lv * kLog2e;
+      if (p.delta_ready) dlt[r] = p.delta[(size_t)head * p.tq + l_row0 + qr[r]];
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      qf[r][s] = row_ok[r] ? *reinterpret_cast<const bf16x8*>(p.q + o_off[r] + 32 * s + 8 * g4) : bf16x8{};
+      dof[r][s] = row_ok[r] ? *reinterpret_cast<const bf16x8*>(p.d_o + o_off[r] + 32 * s + 8 * g4) : bf16x8{};
+    }
   }
   // Delta = rowsum(dO * O) for this row and head, unless the caller supplied
-  // it: this lane's half of the row (d = 16 s + 8 hh .. +8) from the dO
-  // operands already in registers, then the lane pair's sum.  Each (row,
-  // head) belongs to exactly one dQ work item, which stores it for the dK/dV
-  // kernel that runs next.
+  // it: this lane's quarter of the row (d = 32 s + 8 g .. +8) from the dO
+  // operands already in registers, then the sum over the row's four lanes.
+  // Each (row, head) belongs to exactly one dQ work item, which stores it for
+  // the dK/dV kernel that runs next.
   if (!p.delta_ready) {
-    float part = 0.f;
-    if (row_ok) {
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + o_off + 16 * s + 8 * hh);
+    for (int r = 0; r < 2; ++r) {
+      float part = 0.f;
+      if (row_ok[r]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)ov[e], (float)dof[s][e], part);
+        for (int s = 0; s < NKS; ++s) {
+          const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + o_off[r] + 32 * s + 8 * g4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)ov[e], (float)dof[r][s][e], part);
+        }
       }
+      part += __shfl_xor(part, 16);
+      dlt[r] = pair_sum32(part);
+      if (row_ok[r] && g4 == 0) p.delta[(size_t)head * p.tq + l_row0 + qr[r]] = dlt[r];
     }
-    dlt = pair_sum32(part);
-    if (row_ok && hh == 0) p.delta[(size_t)head * p.tq + l_row0 + qr] = dlt;
   }
-  f32x16 dqacc[NDB];
+  // dQ^T accumulators: d block b, row half r; lane group g holds d = dcol(b, g) .. +3
+  f32x4 dqacc[NDB][2];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) dqacc[b] = f32x16{};
-  // -Delta of this lane's row in every accumulator entry: the initial dP^T
-  f32x16 ndlt;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) ndlt[r] = -dlt;
-
-  // transpose-read source row/column for the K^T operand (keys in the S^T
-  // accumulator's permuted order, see the forward kernel)
-  const int i16 = lane & 15;
-  const int kt_row = 4 * hh + (i16 >> 2), kt_col = 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  for (int b = 0; b < NDB; ++b) dqacc[b][0] = dqacc[b][1] = f32x4{};
 
   wait_vmem();
   __syncthreads();
-  // K reads: a lane byte offset inside the tile (row ln or kt_row (+ 8),
-  // column block) plus a constant (buffer, 32-key block, 16-key step) in the
-  // instruction's offset field; the swizzle repeats every 16 rows
+  // K and V operand reads of S^T / dP^T: row 16 kb + (l mod 16), d = 32 s +
+  // 8 g .. +8; a lane byte offset inside the tile plus a constant (buffer,
+  // 16-key block, k-step) in the instruction's offset field (the K swizzle
+  // repeats every 16 rows)
   constexpr int KRB = L::kRowElems * 2;                 // bytes per K row
   const char* kb_s = reinterpret_cast<const char*>(&k_s[0][0]);
-  uint32_t ko[NKS], kto[NDB][2];
+  uint32_t ko[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) ko[s] = 2u * (uint32_t)L::off(ln, 16 * s + 8 * hh);
+  for (int s = 0; s < NKS; ++s) ko[s] = 2u * (uint32_t)L::off(i16, 32 * s + 8 * g4);
+  // K^T operand of dQ^T += K^T dS^T (transpose reads, see lds_read_tr16): d
+  // block b covers the 8-column chunks c(b) and c(b) + 2, c(b) = 4 (b / 2) +
+  // b mod 2 (with the K swizzle, chunks two apart keep the 8 rows x 4 column
+  // groups of a 32-lane read on distinct banks); as the supplier of group g,
+  // lane l names key row 4 g + (l mod 16) / 4 and column group (l mod 4) of
+  // the block, so lane l of the group receives keys 4 g .. 4 g + 3 of the
+  // block's column (l mod 16).  The second read of a 32-key half takes the
+  // keys 16 rows further (the dS^T operand's key order, as in the forward).
+  auto dcol = [](int b, int c) { const int ch = 4 * (b >> 1) + (b & 1) + 2 * (c >> 1); return 8 * ch + 4 * (c & 1); };
+  uint32_t kto[NDB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b)
-#pragma unroll
-    for (int o = 0; o < 2; ++o) kto[b][o] = 2u * (uint32_t)L::off(kt_row + 8 * o, 32 * b + kt_col);
+  for (int b = 0; b < NDB; ++b) kto[b] = 2u * (uint32_t)L::off(4 * g4 + (i16 >> 2), dcol(b, i16 & 3));
   // One KV tile (index u); the K / V buffer is a compile-time constant so
   // that LDS addresses fold into immediates.
   auto tile_step = [&](int u, auto buf_c) __attribute__((always_inline)) {
@@ -724,45 +747,68 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     const uint16_t* vs = v_s[buf];
     const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // the S / dP MFMAs at raised wave priority (the other wave of the SIMD
-      // fills the gaps with its vector work)
+    for (int t = 0; t < 2; ++t) {
+      // S^T and dP^T of the 32 keys 32 t .. +31 (16-key blocks kb = 2 t, 2 t + 1)
+      // at raised wave priority (the other wave of the SIMD fills the gaps
+      // with its vector work); dP^T starts from -Delta, so dS^T = P^T dP^T
       __builtin_amdgcn_s_setprio(1);
-      f32x16 sacc = f32x16{}, dpacc = ndlt;          // dP^T starts from -Delta: dS^T = P^T dP^T
+      f32x4 sacc[2][2], dpacc[2][2];
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb_s + ko[s] + (KB0 + 32 * kb * KRB));
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[(32 * kb + ln) * VS + 16 * s + 8 * hh]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc, 0, 0, 0);
-      }
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          sacc[k][r] = f32x4{};
+          dpacc[k][r] = f32x4{-dlt[r], -dlt[r], -dlt[r], -dlt[r]};
+        }
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int kb = 2 * t + k;
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb_s + ko[s] + (KB0 + 16 * kb * KRB));
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[(16 * kb + i16) * VS + 32 * s + 8 * g4]);
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            sacc[k][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[r][s], sacc[k][r], 0, 0, 0);
+            dpacc[k][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dof[r][s], dpacc[k][r], 0, 0, 0);
+          }
+        }
       __builtin_amdgcn_s_setprio(0);
       // document mask (PARTIAL and ragged tiles only, a wave-uniform branch):
       // masked scores become -inf, so P = 0
       if (partial) {
-        const int rel0 = p.kv_lo + kt * BK + 32 * kb + 4 * hh - a_lo;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((unsigned)(rel0 + 8 * (r >> 2) + (r & 3)) > (unsigned)a_w) sacc[r] = -INFINITY;
-      }
-      // P^T and dS^T for keys 32 kb + 8 (r / 4) + 4 hh + r % 4 of this tile
-      float ds[16];
+        for (int r = 0; r < 2; ++r) {
+          const int rel0 = p.kv_lo + kt * BK + 32 * t + 4 * g4 - a_lo[r];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.scale_log2, -lse2));
-        ds[r] = pr * dpacc[r];
-      }
+          for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8 dsb = cvt8(ds[8 * k2], ds[8 * k2 + 1], ds[8 * k2 + 2], ds[8 * k2 + 3], ds[8 * k2 + 4],
-                                ds[8 * k2 + 5], ds[8 * k2 + 6], ds[8 * k2 + 7]);
-#pragma unroll
-        for (int b = 0; b < NDB; ++b) {
-          const int rows_b = (32 * kb + 16 * k2) * KRB;
-          const bf16x8 kT = tr_operand(reinterpret_cast<const uint16_t*>(kb_s + kto[b][0] + (KB0 + rows_b)),
-                                       reinterpret_cast<const uint16_t*>(kb_s + kto[b][1] + (KB0 + rows_b)));
-          dqacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsb, dqacc[b], 0, 0, 0);
+            for (int e = 0; e < 4; ++e)
+              if ((unsigned)(rel0 + 16 * k + e) > (unsigned)a_w[r]) sacc[k][r][e] = -INFINITY;
         }
+      }
+      // P^T and dS^T of keys 32 t + 16 k + 4 g + e; the dS^T operand of row
+      // half r in the key order {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3}
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        float ds[8];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k][r][e], p.scale_log2, -lse2[r]));
+            ds[4 * k + e] = pr * dpacc[k][r][e];
+          }
+        dsb[r] = cvt8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      }
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) {
+        const char* kp = kb_s + kto[b] + (KB0 + 32 * t * KRB);
+        const bf16x8 kT = tr_operand(reinterpret_cast<const uint16_t*>(kp),
+                                     reinterpret_cast<const uint16_t*>(kp + 16 * KRB));
+        dqacc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kT, dsb[0], dqacc[b][0], 0, 0, 0);
+        dqacc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kT, dsb[1], dqacc[b][1], 0, 0, 0);
       }
     }
     wait_vmem();
@@ -773,22 +819,21 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     if (u + 1 < n) tile_step(u + 1, std::integral_constant<int, 1>{});
   }
 
-  // dQ = scale * acc: lane's row, d = 32 b + 8 g + 4 hh .. +4 (added to dq for split-KV callers)
-  if (row_ok) {
-    float* dqp = p.dq + o_off + 4 * hh;
+  // dQ = scale * acc: row 16 r + l mod 16, d = dcol(b, g) .. +4 (added to dq for split-KV callers)
 #pragma unroll
-    for (int b = 0; b < NDB; ++b)
+  for (int r = 0; r < 2; ++r) {
+    if (!row_ok[r]) continue;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float4 val = make_float4(dqacc[b][4 * g4] * p.scale, dqacc[b][4 * g4 + 1] * p.scale,
-                                 dqacc[b][4 * g4 + 2] * p.scale, dqacc[b][4 * g4 + 3] * p.scale);
-        float4* dst = reinterpret_cast<float4*>(dqp + 32 * b + 8 * g4);
-        if (p.accumulate_dq) {
-          const float4 old = *dst;
-          val.x += old.x; val.y += old.y; val.z += old.z; val.w += old.w;
-        }
-        *dst = val;
+    for (int b = 0; b < NDB; ++b) {
+      float4 val = make_float4(dqacc[b][r][0] * p.scale, dqacc[b][r][1] * p.scale, dqacc[b][r][2] * p.scale,
+                               dqacc[b][r][3] * p.scale);
+      float4* dst = reinterpret_cast<float4*>(p.dq + o_off[r] + dcol(b, g4));
+      if (p.accumulate_dq) {
+        const float4 old = *dst;
+        val.x += old.x; val.y += old.y; val.z += old.z; val.w += old.w;
       }
+      *dst = val;
+    }
   }
 }
 
