@@ -571,24 +571,24 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   constexpr int NW = RB * HB;           // waves per workgroup (two workgroups per CU)
   static_assert(NW == 4, "four waves per workgroup");
   constexpr int BK = kDqBK;
-  using L = SwzTile<D>;                 // K tile: row chunks and transpose reads
-  constexpr int VS = D + 8;             // V tile: row chunks only (padded rows)
+  using L = SwzTile<D>;                 // K and V tiles (K: row chunks and transpose reads; V: row chunks)
   constexpr int CPK = D / 8;
   constexpr int NKS = D / 32;           // 32-wide k-steps of S^T and dP^T
   constexpr int NDB = D / 16;           // 16-wide d blocks of dQ
   // K and V tiles reach LDS by direct global-to-LDS loads: a tile is a run of
-  // 16-byte slots (SK / SV per row: the row's chunks plus padding slots), and
+  // 16-byte slots (SK per row: the row's chunks plus any padding slots), and
   // direct load j fills slots 64 j .. 64 j + 63.  Lane l of load j maps slot
-  // q = 64 j + l back to (row q / S, stored position q % S): K chunk
-  // position ^ f(row) (unpadded swizzled rows), V chunk = position; padding
-  // slots load any real chunk of the row (never read).
-  constexpr int SK = L::kRowElems / 8, SV = VS / 8;
-  constexpr int WK = BK * SK / 64, WV = BK * SV / 64;       // direct loads per K / V tile
-  constexpr int DK = (WK + NW - 1) / NW, DV = (WV + NW - 1) / NW;   // per wave (the last may be idle)
-  static_assert(BK * SK % 64 == 0 && BK * SV % 64 == 0, "tiles are whole direct loads");
-  constexpr int KTB = BK * SK * 16, VTB = BK * SV * 16;     // bytes per K / V tile
+  // q = 64 j + l back to (row q / SK, stored position q % SK): chunk position
+  // ^ f(row) for D = 128 (unpadded swizzled rows), the position itself for
+  // D = 64; padding slots load any real chunk of the row (never read).  K and
+  // V share the layout, so one set of lane offsets serves both.
+  constexpr int SK = L::kRowElems / 8;
+  constexpr int WK = BK * SK / 64;                          // direct loads per K or V tile
+  constexpr int DK = (WK + NW - 1) / NW;                    // per wave (the last may be idle)
+  static_assert(BK * SK % 64 == 0, "tiles are whole direct loads");
+  constexpr int KTB = BK * SK * 16;                         // bytes per K or V tile
   __shared__ __attribute__((aligned(16))) uint16_t k_s[2][L::kElems(BK)];
-  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][BK * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_s[2][L::kElems(BK)];
 
   if (p.err[0]) return;
 
@@ -623,18 +623,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)(kv_rstride * sizeof(uint16_t));
   // lane source offsets (bytes from the tile's first row) of this wave's loads
-  uint32_t krow[DK], kchk[DK], vrow[DV], vchk[DV];
+  uint32_t krow[DK], kchk[DK];
 #pragma unroll
   for (int i = 0; i < DK; ++i) {
     const int q = (wave_u + NW * i) * 64 + lane, r = q / SK, pos = q % SK;
     krow[i] = (uint32_t)r * row_bytes;
     kchk[i] = 16u * (uint32_t)(D == 128 ? (pos ^ L::f(r)) : min(pos, CPK - 1));
-  }
-#pragma unroll
-  for (int i = 0; i < DV; ++i) {
-    const int q = (wave_u + NW * i) * 64 + lane;
-    vrow[i] = (uint32_t)(q / SV) * row_bytes;
-    vchk[i] = 16u * (uint32_t)min(q % SV, CPK - 1);
   }
   const uint32_t k_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&k_s[0][0] + 1024u * wave_u;
   const uint32_t v_wave = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&v_s[0][0] + 1024u * wave_u;
@@ -651,10 +645,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
       if (NW * (i + 1) <= WK || wave_u + NW * i < WK)    // only the last load may be idle
         lds_dma16_so<(uint32_t)(buf * KTB + NW * 1024 * i)>(kb, min(krow[i], lim) + kchk[i], k_wave);
     });
-    static_for<DV>([&](auto ic) __attribute__((always_inline)) {
+    static_for<DK>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (NW * (i + 1) <= WV || wave_u + NW * i < WV)
-        lds_dma16_so<(uint32_t)(buf * VTB + NW * 1024 * i)>(vb, min(vrow[i], lim) + vchk[i], v_wave);
+      if (NW * (i + 1) <= WK || wave_u + NW * i < WK)
+        lds_dma16_so<(uint32_t)(buf * KTB + NW * 1024 * i)>(vb, min(krow[i], lim) + kchk[i], v_wave);
     });
   };
   // the first K / V tile is in flight while the row operands load
@@ -707,7 +701,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
       if (row_ok[r] && g4 == 0) p.delta[(size_t)head * p.tq + l_row0 + qr[r]] = dlt[r];
     }
   }
-  // dQ^T accumulators: d block b, row half r; lane group g holds d = dcol(b, g) .. +3
+  // dQ^T accumulators: d block b, row half r; lane group g holds d = 16 b + 4 g .. +3
   f32x4 dqacc[NDB][2];
 #pragma unroll
   for (int b = 0; b < NDB; ++b) dqacc[b][0] = dqacc[b][1] = f32x4{};
@@ -715,36 +709,33 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   wait_vmem();
   __syncthreads();
   // K and V operand reads of S^T / dP^T: row 16 kb + (l mod 16), d = 32 s +
-  // 8 g .. +8; a lane byte offset inside the tile plus a constant (buffer,
-  // 16-key block, k-step) in the instruction's offset field (the K swizzle
-  // repeats every 16 rows)
+  // 8 g .. +8; one lane byte offset per k-step (the same in the K and V
+  // tiles) plus a constant (buffer, 16-key block) in the instruction's offset
+  // field (the swizzle repeats every 16 rows)
   constexpr int KRB = L::kRowElems * 2;                 // bytes per K row
   const char* kb_s = reinterpret_cast<const char*>(&k_s[0][0]);
+  const char* vb_s = reinterpret_cast<const char*>(&v_s[0][0]);
   uint32_t ko[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) ko[s] = 2u * (uint32_t)L::off(i16, 32 * s + 8 * g4);
-  // K^T operand of dQ^T += K^T dS^T (transpose reads, see lds_read_tr16): d
-  // block b covers the 8-column chunks c(b) and c(b) + 2, c(b) = 4 (b / 2) +
-  // b mod 2 (with the K swizzle, chunks two apart keep the 8 rows x 4 column
-  // groups of a 32-lane read on distinct banks); as the supplier of group g,
-  // lane l names key row 4 g + (l mod 16) / 4 and column group (l mod 4) of
-  // the block, so lane l of the group receives keys 4 g .. 4 g + 3 of the
-  // block's column (l mod 16).  The second read of a 32-key half takes the
-  // keys 16 rows further (the dS^T operand's key order, as in the forward).
-  auto dcol = [](int b, int c) { const int ch = 4 * (b >> 1) + (b & 1) + 2 * (c >> 1); return 8 * ch + 4 * (c & 1); };
+  // K^T operand of dQ^T += K^T dS^T (transpose reads, see lds_read_tr16): as
+  // the supplier of group g, lane l names key row 4 g + (l mod 16) / 4 and
+  // column 16 b + 4 (l mod 4), so lane l of the group receives keys 4 g ..
+  // 4 g + 3 of column 16 b + (l mod 16).  The second read of a 32-key half
+  // takes the keys 16 rows further (the dS^T operand's key order, as in the
+  // forward).
   uint32_t kto[NDB];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) kto[b] = 2u * (uint32_t)L::off(4 * g4 + (i16 >> 2), dcol(b, i16 & 3));
+  for (int b = 0; b < NDB; ++b) kto[b] = 2u * (uint32_t)L::off(4 * g4 + (i16 >> 2), 16 * b + 4 * (i16 & 3));
   // One KV tile (index u); the K / V buffer is a compile-time constant so
   // that LDS addresses fold into immediates.
   auto tile_step = [&](int u, auto buf_c) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
-    constexpr int KB0 = buf * L::kElems(BK) * 2;          // byte offset of this K buffer
+    constexpr int KB0 = buf * L::kElems(BK) * 2;          // byte offset of this K (and V) buffer
     const int kt = kt_lo + u;
     // the next tile into the other buffer (its last reader finished before
     // the previous barrier); in flight during this tile's math
     if (u + 1 < n) issue_tile(kt + 1, std::integral_constant<int, buf ^ 1>{});
-    const uint16_t* vs = v_s[buf];
     const bool partial = kt < kt_flo || kt >= kt_fhi || (kt + 1) * BK > tkv;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -766,7 +757,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         for (int k = 0; k < 2; ++k) {
           const int kb = 2 * t + k;
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb_s + ko[s] + (KB0 + 16 * kb * KRB));
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[(16 * kb + i16) * VS + 32 * s + 8 * g4]);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb_s + ko[s] + (KB0 + 16 * kb * KRB));
 #pragma unroll
           for (int r = 0; r < 2; ++r) {
             sacc[k][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[r][s], sacc[k][r], 0, 0, 0);
@@ -819,7 +810,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     if (u + 1 < n) tile_step(u + 1, std::integral_constant<int, 1>{});
   }
 
-  // dQ = scale * acc: row 16 r + l mod 16, d = dcol(b, g) .. +4 (added to dq for split-KV callers)
+  // dQ = scale * acc: row 16 r + l mod 16, d = 16 b + 4 g .. +4 (added to dq for split-KV callers)
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     if (!row_ok[r]) continue;
@@ -827,7 +818,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     for (int b = 0; b < NDB; ++b) {
       float4 val = make_float4(dqacc[b][r][0] * p.scale, dqacc[b][r][1] * p.scale, dqacc[b][r][2] * p.scale,
                                dqacc[b][r][3] * p.scale);
-      float4* dst = reinterpret_cast<float4*>(p.dq + o_off[r] + dcol(b, g4));
+      float4* dst = reinterpret_cast<float4*>(p.dq + o_off[r] + 16 * b + 4 * g4);
       if (p.accumulate_dq) {
         const float4 old = *dst;
         val.x += old.x; val.y += old.y; val.z += old.z; val.w += old.w;

@@ -137,18 +137,24 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
 }
 
 // Row-major bf16 tiles in LDS that are read both as 16-byte row chunks (MFMA
-// operands along the row) and through transpose reads (operands down the
-// columns).  For D = 128 rows are unpadded and the 16 chunks of row r are
-// stored at chunk position c ^ f(r), with f a bijection of r mod 16, so that
-// 16 consecutive rows reading one chunk, and 32 lanes reading 4 rows x 64 B
-// through transpose reads, touch distinct banks:
-//   f(r) = 4 (r mod 4) + (r / 4 mod 4).
-// For D = 64 rows are padded by 16 bytes instead.
+// operands along the row; lane l reads row l mod 16 at chunk l / 16 (+ 4 s))
+// and through transpose reads (operands down the columns; the lanes of group
+// g = l / 16 name rows 4 g + (l mod 16) / 4 at column groups l mod 4 of 16
+// consecutive columns).  The LDS serves a 16-byte read in 16-lane cycles and a
+// transpose read in 32-lane cycles whose lane sets are not consecutive lanes;
+// the layouts below were measured bank-conflict free for both patterns
+// (SQ_LDS_BANK_CONFLICT), where the swizzle f(r) = 4 (r mod 4) + (r / 4 mod 4)
+// conflicts on the 16-byte reads and f(r) = r mod 16 on the transpose reads.
+// For D = 128 rows are unpadded and the 16 chunks of row r are stored at
+// chunk position c ^ f(r), f a function of r mod 16 (the layout repeats every
+// 16 rows):
+//   f(r) = 2 ((r' ^ (r' >> 3)) mod 8),  r' = r mod 16.
+// For D = 64 rows are padded to 80 elements (160 bytes) instead.
 template <int D>
 struct SwzTile {
-  static constexpr int kRowElems = D == 128 ? 128 : D + 8;
+  static constexpr int kRowElems = D == 128 ? 128 : D + 16;
   static constexpr int kElems(int rows) { return rows * kRowElems; }
-  __device__ static __forceinline__ int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+  __device__ static __forceinline__ int f(int r) { const int q = r & 15; return ((q ^ (q >> 3)) & 7) << 1; }
   // element offset of (row r, column col); col % 4 == 0 for transpose reads
   __device__ static __forceinline__ int off(int r, int col) {
     if (D == 128) return r * 128 + (((col >> 3) ^ f(r)) << 3) + (col & 7);

@@ -52,7 +52,7 @@ template <int D, int RB, int HB>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   static_assert(RB * HB == 4, "four waves per workgroup");
   constexpr int BK = kFwdBK;
-  constexpr int KSTR = D + 8;           // K row stride (bf16): 16-byte row reads of 16 rows hit distinct banks
+  constexpr int KSTR = D + 16;          // K row stride (bf16): the 16-byte row reads hit distinct banks
   constexpr int VSTR = D + 16;          // V row stride: transpose reads of 8 rows x 4 columns hit distinct banks
   constexpr int CPK = D / 8;            // 16-byte chunks per key row
   constexpr int KCH = KSTR / 8, VCH = VSTR / 8;       // 16-byte slots per LDS row (data + padding)
