@@ -22,7 +22,7 @@ During the timed steps the library's event timer brackets every kernel
 launch on its stream; the roofline line is the kernel with the largest share
 of the step: its algorithmic flop per launch divided by its mean launch time.
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--cp-backward] [--study sharding|length]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline] [--cp-backward] [--study sharding|length|power]
 """
 from __future__ import annotations
 
@@ -413,10 +413,11 @@ def study_power(seconds: float = 4.0):
     """Board power and GFX clocks (amd-smi, sampled about every 0.3 s) while
     the step's forward, its backward and, as references of what the chip
     sustains on pure matrix work, a bf16 8192^3 GEMM (torch.matmul) and the
-    library's matrix-core probe (back-to-back v_mfma_f32_32x32x16_bf16 on
-    operands in registers, no memory traffic; N(0, 1) bf16 operands, and all
-    zeros as a control for data-dependent power) each run back to back for
-    `seconds`; one JSON line with the medians per phase."""
+    library's matrix-core probe (back-to-back v_mfma_f32_32x32x16_bf16, then
+    v_mfma_f32_16x16x32_bf16, on operands in registers, no memory traffic;
+    N(0, 1) bf16 operands, and all zeros as a control for data-dependent
+    power) each run back to back for `seconds`; one JSON line with the
+    medians per phase."""
     import statistics
     import subprocess
     import threading
@@ -465,7 +466,11 @@ def study_power(seconds: float = 4.0):
              10.0 * w.d * w.hq * pairs),
             ("gemm_bf16_8192", lambda: torch.matmul(a, b), 2.0 * 8192 ** 3),
             ("mfma_probe_randn", lambda: api.mfma_probe(probe_ops, probe_wg, probe_iters, out=probe_out), probe_flop),
-            ("mfma_probe_zero", lambda: api.mfma_probe(probe_zero, probe_wg, probe_iters, out=probe_out), probe_flop))
+            ("mfma_probe_zero", lambda: api.mfma_probe(probe_zero, probe_wg, probe_iters, out=probe_out), probe_flop),
+            ("mfma16_probe_randn", lambda: api.mfma_probe(probe_ops, probe_wg, probe_iters, out=probe_out, shape=16),
+             probe_flop),
+            ("mfma16_probe_zero", lambda: api.mfma_probe(probe_zero, probe_wg, probe_iters, out=probe_out, shape=16),
+             probe_flop))
     for _, fn, _ in legs:
         fn()
     torch.cuda.synchronize()

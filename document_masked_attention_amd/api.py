@@ -65,7 +65,7 @@ _SIGNATURES = {
     "docmask_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "docmask_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "docmask_kernel_class_name": (ctypes.c_char_p, [ctypes.c_int]),
-    "docmask_mfma_probe": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
+    "docmask_mfma_probe": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i32, _vp, _vp]),
     "docmask_plan_shards": (ctypes.c_int, [_vp, _i32, _i32, ctypes.c_double, _vp, _i32, _vp, _vp,
                                            ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)]),
     "docmask_copy_rows": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _i32, ctypes.c_int, _vp]),
@@ -316,14 +316,15 @@ def kernel_class_name(kernel_class: int) -> str:
 PROBE_FLOP_PER_WAVE_ITER = 32768 * 16     # 16 v_mfma_f32_32x32x16_bf16 per loop iteration
 
 
-def mfma_probe(operands: torch.Tensor, n_workgroups: int, iters: int, out=None) -> torch.Tensor:
-    """docmask_mfma_probe: back-to-back bf16 MFMAs on `operands` (a bf16
-    device tensor) in n_workgroups x 4 waves; float32 [256 n_workgroups], one
-    sum of accumulator elements per lane."""
+def mfma_probe(operands: torch.Tensor, n_workgroups: int, iters: int, out=None, shape: int = 32) -> torch.Tensor:
+    """docmask_mfma_probe: back-to-back bf16 MFMAs (shape 32: 32 x 32 x 16,
+    shape 16: 16 x 16 x 32) on `operands` (a bf16 device tensor) in
+    n_workgroups x 4 waves; float32 [256 n_workgroups], one sum of
+    accumulator elements per lane."""
     operands = _bits(operands)
     if out is None:
         out = torch.empty(256 * n_workgroups, dtype=torch.float32, device=operands.device)
-    st = lib().docmask_mfma_probe(_ptr(operands), operands.numel(), n_workgroups, iters, _ptr(out), _stream())
+    st = lib().docmask_mfma_probe(_ptr(operands), operands.numel(), n_workgroups, iters, shape, _ptr(out), _stream())
     _check(st, "docmask_mfma_probe")
     return out
 

@@ -339,21 +339,26 @@ const char* docmask_kernel_class_name(int kernel_class);
 /* Matrix-core rate probe (instrumentation; defines no attention operation).
  * Measures what the matrix cores sustain on given bf16 data: n_workgroups
  * workgroups of 4 waves (at most two resident per compute unit) each run `iters`
- * iterations of 16 v_mfma_f32_32x32x16_bf16 -- the instruction of the
- * attention kernels -- on operands held in registers, with no other memory
- * traffic.  Lane gl (global thread index) loads its 8 A and 8 B operand
- * registers once, 8 bf16 values each, from `operands` (device, n_operands
- * values, 16-byte aligned): A slot j at (128 gl + 8 j) mod n_operands, B slot
- * j at (128 gl + 64 + 8 j) mod n_operands; MFMA k of an iteration multiplies
- * A slot k mod 8 (the 32 x 16 operand: lane l holds row l mod 32, columns
- * 8 (l / 32) .. +8) by B slot 3k mod 8 (16 x 32: lane l holds column l mod 32,
- * rows 8 (l / 32) .. +8) into accumulator k mod 4.  Each lane writes the sum
- * of its accumulator elements to out[gl] (device float, 256 n_workgroups
- * entries).  Work per call: 32768 * 16 * iters * 4 * n_workgroups flop.
- * Asynchronous on `stream`; DOCMASK_EINVAL for null or misaligned pointers,
- * n_operands < 128 or not a multiple of 8, n_workgroups < 1, iters < 0. */
-int docmask_mfma_probe(const void* operands, int64_t n_operands, int32_t n_workgroups, int32_t iters, float* out,
-                       hipStream_t stream);
+ * iterations of back-to-back bf16 MFMAs on operands held in registers, with no
+ * other memory traffic.  shape 32: 16 v_mfma_f32_32x32x16_bf16 per iteration
+ * (the dK/dV kernel's instruction) into accumulator k mod 4; shape 16: 32
+ * v_mfma_f32_16x16x32_bf16 (the forward's and the dQ kernel's) into
+ * accumulator k mod 8; the same 2^19 products per wave and iteration.  Lane
+ * gl (global thread index) loads its 8 A and 8 B operand registers once, 8
+ * bf16 values each, from `operands` (device, n_operands values, 16-byte
+ * aligned): A slot j at (128 gl + 8 j) mod n_operands, B slot j at (128 gl +
+ * 64 + 8 j) mod n_operands; MFMA k of an iteration multiplies A slot k mod 8
+ * by B slot 3k mod 8.  Operand layouts: 32 x 16 A, lane l holds row l mod 32,
+ * columns 8 (l / 32) .. +8, and 16 x 32 B, column l mod 32, rows 8 (l / 32)
+ * .. +8 (shape 32); 16 x 32 A, row l mod 16, columns 8 (l / 16) .. +8, and
+ * 32 x 16 B, column l mod 16, rows 8 (l / 16) .. +8 (shape 16).  Each lane
+ * writes the sum of its accumulator elements to out[gl] (device float, 256
+ * n_workgroups entries).  Work per call: 32768 * 16 * iters * 4 *
+ * n_workgroups flop.  Asynchronous on `stream`; DOCMASK_EINVAL for null or
+ * misaligned pointers, n_operands < 128 or not a multiple of 8, n_workgroups
+ * < 1, iters < 0, a shape other than 32 or 16. */
+int docmask_mfma_probe(const void* operands, int64_t n_operands, int32_t n_workgroups, int32_t iters, int32_t shape,
+                       float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

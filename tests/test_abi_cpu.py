@@ -150,14 +150,16 @@ def test_timing_controls(lib):
 
 def test_mfma_probe_validation(lib):
     probe = lib.docmask_mfma_probe
-    assert probe(None, 1024, 1, 1, FAKE, None) == api.EINVAL
-    assert probe(FAKE, 1024, 1, 1, None, None) == api.EINVAL
-    assert probe(MIS, 1024, 1, 1, FAKE, None) == api.EINVAL            # operands not 16-byte aligned
-    assert probe(FAKE, 1024, 1, 1, FAKE + 2, None) == api.EINVAL       # out not 4-byte aligned
-    assert probe(FAKE, 120, 1, 1, FAKE, None) == api.EINVAL            # fewer than 128 values
-    assert probe(FAKE, 1028, 1, 1, FAKE, None) == api.EINVAL           # not a multiple of 8
-    assert probe(FAKE, 1024, 0, 1, FAKE, None) == api.EINVAL
-    assert probe(FAKE, 1024, 1, -1, FAKE, None) == api.EINVAL
+    assert probe(None, 1024, 1, 1, 32, FAKE, None) == api.EINVAL
+    assert probe(FAKE, 1024, 1, 1, 32, None, None) == api.EINVAL
+    assert probe(MIS, 1024, 1, 1, 32, FAKE, None) == api.EINVAL        # operands not 16-byte aligned
+    assert probe(FAKE, 1024, 1, 1, 32, FAKE + 2, None) == api.EINVAL   # out not 4-byte aligned
+    assert probe(FAKE, 120, 1, 1, 32, FAKE, None) == api.EINVAL        # fewer than 128 values
+    assert probe(FAKE, 1028, 1, 1, 32, FAKE, None) == api.EINVAL       # not a multiple of 8
+    assert probe(FAKE, 1024, 0, 1, 32, FAKE, None) == api.EINVAL
+    assert probe(FAKE, 1024, 1, -1, 32, FAKE, None) == api.EINVAL
+    for shape in (0, 8, 24, 64):                                       # only 32 and 16
+        assert probe(FAKE, 1024, 1, 1, shape, FAKE, None) == api.EINVAL
 
 
 def _copy(lib, maps=((0, 0, 4),), src_k=FAKE, src_v=FAKE, dst_k=FAKE, dst_v=FAKE, src_rows=10, dst_rows=10,
