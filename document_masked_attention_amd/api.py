@@ -313,7 +313,7 @@ def kernel_class_name(kernel_class: int) -> str:
     return lib().docmask_kernel_class_name(kernel_class).decode()
 
 
-PROBE_FLOP_PER_WAVE_ITER = 32768 * 16     # 16 v_mfma_f32_32x32x16_bf16 per loop iteration
+PROBE_FLOP_PER_WAVE_ITER = 32768 * 16     # per wave and loop iteration, either shape (16 MFMAs of 32x32x16 or 32 of 16x16x32)
 
 
 def mfma_probe(operands: torch.Tensor, n_workgroups: int, iters: int, out=None, shape: int = 32) -> torch.Tensor:
