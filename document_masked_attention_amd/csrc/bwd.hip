@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // and the LDS reads of slot k + PF, so every operand has PF slots of
   // matrix work to arrive.
   constexpr int NP = 4 * NMB;           // == 2 * NKS: slots per region
-  constexpr int PF = 2;                 // operand prefetch distance (slots)
+  constexpr int PF = 1;                 // operand prefetch distance (slots): 1 measured faster than 2 or 3
   constexpr int EPS = 16 / NP;          // softmax elements per slot
   // Buffers GA (unit ja: dV / dK operands), GB (unit jb: S / dP operands)
   // and GC (unit jc: softmax LSE) are compile-time ring indices.
