@@ -52,17 +52,17 @@ template <int D, int RB, int HB>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   static_assert(RB * HB == 4, "four waves per workgroup");
   constexpr int BK = kFwdBK;
-  constexpr int KSTR = D + 16;          // K row stride (bf16): the 16-byte row reads hit distinct banks
-  constexpr int VSTR = D + 16;          // V row stride: transpose reads of 8 rows x 4 columns hit distinct banks
+  using L = SwzTile<D>;                 // K and V tile layout: 16-byte row reads and transpose reads on distinct banks
   constexpr int CPK = D / 8;            // 16-byte chunks per key row
-  constexpr int KCH = KSTR / 8, VCH = VSTR / 8;       // 16-byte slots per LDS row (data + padding)
-  constexpr int WLK = BK * KCH / 64, WLV = BK * VCH / 64;   // direct loads (64 slots) per tile
-  static_assert(BK * KCH % 64 == 0 && BK * VCH % 64 == 0, "tiles are whole direct loads");
-  constexpr int DPK = (WLK + 3) / 4, DPV = (WLV + 3) / 4;   // per wave (the last may be idle)
+  constexpr int RE = L::kRowElems;      // LDS row length (bf16): D = 128 unpadded, D = 64 padded to 80
+  constexpr int SK = RE / 8;            // 16-byte slots per LDS row
+  constexpr int WL = BK * SK / 64;      // direct loads (64 slots) per K or V tile
+  static_assert(BK * SK % 64 == 0, "tiles are whole direct loads");
+  constexpr int DP = (WL + 3) / 4;      // per wave (the last may be idle)
   constexpr int NKS = D / 32;           // 32-wide k-steps of QK^T
   constexpr int NDB = D / 16;           // 16-wide d blocks of O
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BK * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][L::kElems(BK)];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][L::kElems(BK)];
 
   if (p.err[0]) return;
 
@@ -111,28 +111,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const uint16_t* kbase = p.k + (size_t)kvh * D;
   const uint16_t* vbase = p.v + (size_t)kvh * D;
   // K and V tiles reach LDS by direct global-to-LDS loads (no staging
-  // registers; completion by this wave's vmcnt, then a barrier).  A tile of
-  // padded rows is a run of 16-byte slots; direct load j (of a wave: j = wave
-  // + 4 i) fills slots 64 j .. 64 j + 63, and lane l's slot 64 j + l is row
-  // q / CH, chunk q % CH (q = 64 j + l).  Padding slots load any real chunk
-  // of the row (never read).  The tile base is wave-uniform; each lane adds a
-  // 32-bit byte offset.  Padding keys of a ragged last tile read the last real
-  // row instead: their scores are always masked (P = 0 exactly), so any
-  // finite K/V row will do.
+  // registers; completion by this wave's vmcnt, then a barrier).  A tile is a
+  // run of 16-byte slots, RE / 8 per row; direct load j (of a wave: j = wave
+  // + 4 i) fills slots 64 j .. 64 j + 63, and lane l's slot q = 64 j + l is
+  // position q % SK of row q / SK, which holds the row's chunk of that
+  // position under the tile's swizzle (D = 128), or the same chunk (D = 64;
+  // its padding slots load any real chunk of the row, never read).  K and V
+  // tiles share the layout and so the lane offsets.  The tile base is
+  // wave-uniform; each lane adds a 32-bit byte offset.  Padding keys of a
+  // ragged last tile read the last real row instead: their scores are always
+  // masked (P = 0 exactly), so any finite K/V row will do.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)(kv_rstride * sizeof(uint16_t));
-  uint32_t krow[DPK], kchk[DPK], vrow[DPV], vchk[DPV];
+  uint32_t lrow[DP], lchk[DP];
 #pragma unroll
-  for (int i = 0; i < DPK; ++i) {
-    const int q = (wave_u + 4 * i) * 64 + lane;
-    krow[i] = (uint32_t)(q / KCH) * row_bytes;
-    kchk[i] = 16u * (uint32_t)min(q % KCH, CPK - 1);
-  }
-#pragma unroll
-  for (int i = 0; i < DPV; ++i) {
-    const int q = (wave_u + 4 * i) * 64 + lane;
-    vrow[i] = (uint32_t)(q / VCH) * row_bytes;
-    vchk[i] = 16u * (uint32_t)min(q % VCH, CPK - 1);
+  for (int i = 0; i < DP; ++i) {
+    const int q = (wave_u + 4 * i) * 64 + lane, r = q / SK, pos = q % SK;
+    lrow[i] = (uint32_t)r * row_bytes;
+    lchk[i] = 16u * (uint32_t)(D == 128 ? (pos ^ L::f(r)) : min(pos, CPK - 1));
   }
   // full tiles: uniform tile base + precomputed lane offsets; the ragged last
   // tile clamps the row part of the offset (a wave-uniform branch)
@@ -161,16 +157,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     }
   };
   auto issue_k = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
-    issue_rows(kbase, kt, lds, krow, kchk, std::integral_constant<int, DPK>{}, std::integral_constant<int, WLK>{});
+    issue_rows(kbase, kt, lds, lrow, lchk, std::integral_constant<int, DP>{}, std::integral_constant<int, WL>{});
   };
   auto issue_v = [&](int kt, uint16_t* lds) __attribute__((always_inline)) {
-    issue_rows(vbase, kt, lds, vrow, vchk, std::integral_constant<int, DPV>{}, std::integral_constant<int, WLV>{});
+    issue_rows(vbase, kt, lds, lrow, lchk, std::integral_constant<int, DP>{}, std::integral_constant<int, WL>{});
   };
-  // Transpose-read source address of this lane inside a V tile (see
-  // lds_read_tr16): as the supplier of group g, lane l names row 4 g + (l mod
-  // 16) / 4 and column 4 (l mod 4) of a 16-key x 16-column block, so that
-  // lane l of the group receives rows 4 g .. 4 g + 3 of column l mod 16.
-  const int vt_off = (4 * g4 + (i16 >> 2)) * VSTR + 4 * (i16 & 3);
+  // LDS element offsets of this lane's reads in a tile.  K rows (S^T's A
+  // operand): row 16 kb + (l mod 16), d = 32 s + 8 g .. +8, one offset per
+  // k-step s (the swizzle repeats every 16 rows, so block kb adds 16 kb rows).
+  // V^T (transpose reads, see lds_read_tr16): as the supplier of group g,
+  // lane l names row 4 g + (l mod 16) / 4 and column 16 b + 4 (l mod 4), so
+  // that lane l of the group receives rows 4 g .. 4 g + 3 of column
+  // 16 b + (l mod 16); one offset per 16-column block b, the 32-key half t
+  // and the second read (16 rows on) adding whole rows.
+  int ko[NKS], vto[NDB];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) ko[s] = L::off(i16, 32 * s + 8 * g4);
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) vto[b] = L::off(4 * g4 + (i16 >> 2), 16 * b + 4 * (i16 & 3));
 
   // S^T = K Q^T over the tile held in K buffer kl: 4 blocks of 16 keys x the
   // two 16-row halves, D / 32 k-steps; every K operand feeds both halves
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     bf16x8 op[NT];
     auto load = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      op[i] = *reinterpret_cast<const bf16x8*>(&kl[(16 * (i % 4) + i16) * KSTR + 32 * (i / 4) + 8 * g4]);
+      op[i] = *reinterpret_cast<const bf16x8*>(&kl[ko[i / 4] + 16 * (i % 4) * RE]);
     };
     static_for<PFS>([&](auto ic) __attribute__((always_inline)) { load(ic); });
     static_for<NT>([&](auto ic) __attribute__((always_inline)) {
@@ -326,11 +330,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       auto load = [&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i < NS) {
-          opr[i] = *reinterpret_cast<const bf16x8*>(&kl[(16 * (i % 4) + i16) * KSTR + 32 * (i / 4) + 8 * g4]);
+          opr[i] = *reinterpret_cast<const bf16x8*>(&kl[ko[i / 4] + 16 * (i % 4) * RE]);
         } else {
           constexpr int t = (i - NS) / NDB, b = (i - NS) % NDB;
-          const uint16_t* vp = vl + vt_off + 32 * t * VSTR + 16 * b;
-          opr[i] = tr_operand(vp, vp + 16 * VSTR);
+          const uint16_t* vp = vl + vto[b] + 32 * t * RE;
+          opr[i] = tr_operand(vp, vp + 16 * RE);
         }
       };
       static_for<PF>([&](auto ic) __attribute__((always_inline)) { load(ic); });
